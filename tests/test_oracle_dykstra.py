@@ -1,0 +1,177 @@
+"""Pins for the oracle's entropic Dykstra solver.
+
+Method (pith.science review of TSENOR, "What carries the argument" and "Core
+claim"): the block LP is a capacitated OT problem, regularised by an entropy
+term and solved by Dykstra's alternating KL projections -- row normalisation,
+column normalisation, clip at 1 with its correction term -- in log space.
+Each test below fixes a value by a route independent of the oracle code:
+
+* tau = 0 closed form (uniform N/M), N = M closed form (all ones);
+* bit-exact invariance under scaling W by a power of two;
+* T = 1 written with scipy's logsumexp (C1, then C2, then the clip);
+* when the clip never binds the iteration is textbook Sinkhorn scaling,
+  u = N / (K v), v = N / (K^T u), run in the multiplicative domain;
+* the same iteration in scaling form with the clip as min(., 1) and the
+  correction carried implicitly (derived independently), to 1e-11;
+* the T -> infinity limit equals the KL projection of the Gibbs kernel onto
+  {row sums N, column sums N, 0 <= S <= 1}, computed by maximising its
+  smooth concave dual with L-BFGS (KKT form S = min(1, K e^{a_i + b_j})).
+"""
+import numpy as np
+import pytest
+from scipy.optimize import minimize
+from scipy.special import logsumexp
+
+import oracle
+from sparse_mask_search_amd import workloads as wl
+
+
+def _block_matrix(seed, M, nb=4, kind="normal"):
+    return wl.random_blocks(seed, nb, M, kind)
+
+
+@pytest.mark.parametrize("M,N", [(4, 2), (8, 4), (16, 8), (32, 16), (8, 3)])
+@pytest.mark.parametrize("T", [1, 7])
+def test_tau_zero_uniform(M, N, T):
+    W = _block_matrix(1, M)
+    S64, S32 = oracle.dykstra(W, N, M, 0.0, T)
+    assert np.allclose(S64, N / M, rtol=1e-14, atol=0)
+    assert np.all(S32 == S32.flat[0])
+
+
+@pytest.mark.parametrize("M", [4, 8, 16, 32])
+def test_n_equals_m_all_ones(M):
+    # the only feasible point is the all-ones matrix; the iterates reach it
+    W = _block_matrix(2, M, kind="student_t")
+    S64, _ = oracle.dykstra(W, M, M, 25.0, 1000)
+    assert np.allclose(S64, 1.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("k", [-7, 3, 20])
+def test_power_of_two_scale_invariance(k):
+    W = _block_matrix(3, 8, kind="outlier")
+    a64, a32 = oracle.dykstra(W, 4, 8, 20.0, 30)
+    b64, b32 = oracle.dykstra(W * np.float32(2.0 ** k), 4, 8, 20.0, 30)
+    assert np.array_equal(a64, b64) and np.array_equal(a32, b32)
+
+
+@pytest.mark.parametrize("M,N,tau", [(4, 2, 20.0), (8, 4, 20.0), (16, 8, 30.0), (32, 16, 40.0)])
+def test_range_and_zero_block(M, N, tau):
+    W = _block_matrix(4, M, kind="student_t")
+    W[:, :M] = 0.0  # first block all-zero -> What = 0 -> uniform
+    S64, S32 = oracle.dykstra(W, N, M, tau, 25)
+    assert S64.min() >= 0.0 and S64.max() <= 1.0
+    assert S32.min() >= 0.0 and S32.max() <= 1.0
+    assert np.allclose(S64[:, :M], N / M, rtol=1e-14)
+
+
+def _scores(W, M):
+    B = oracle.block_view(np.abs(W.astype(np.float64)), M)
+    m = B.max(axis=(2, 3), keepdims=True)
+    return np.where(m > 0, B / np.where(m > 0, m, 1), 0.0)
+
+
+@pytest.mark.parametrize("M,N,tau", [(4, 2, 20.0), (8, 4, 20.0), (8, 2, 5.0), (16, 8, 30.0)])
+def test_one_iteration_logsumexp(M, N, tau):
+    W = _block_matrix(5, M, kind="outlier")
+    S64, _ = oracle.dykstra(W, N, M, tau, 1)
+    X = tau * _scores(W, M)
+    X = X - logsumexp(X, axis=3, keepdims=True) + np.log(N)   # C1: rows
+    X = X - logsumexp(X, axis=2, keepdims=True) + np.log(N)   # C2: columns
+    S = np.exp(np.minimum(X, 0.0))                            # C3: clip
+    got = oracle.block_view(S64, M)
+    assert np.allclose(got, S, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("T", [1, 5, 60])
+def test_sinkhorn_when_clip_inactive(T):
+    M, N, tau = 8, 1, 1.0
+    W = _block_matrix(6, M, nb=6)
+    S64, _ = oracle.dykstra(W, N, M, tau, T)
+    K = np.exp(tau * _scores(W, M))  # [bi, bj, M, M]
+    for bj in range(K.shape[1]):
+        k = K[0, bj]
+        v = np.ones(M)
+        for _ in range(T):
+            u = N / (k @ v)
+            v = N / (k.T @ u)
+            S = u[:, None] * k * v[None, :]
+            assert S.max() < 1.0  # the clip never binds in this regime
+        assert np.allclose(S64[:, bj * M:(bj + 1) * M], S, rtol=1e-12, atol=0)
+
+
+def _scaling_form(What, N, tau, T):
+    """Same iteration in scaling form: keep P = exp(Y) with Y = X + Q; each
+    iteration E = min(P U V, 1), a = N / rowsum(E), b = N / colsum(E a),
+    U *= a, V *= b.  (X = min(Y, 0) and Q = max(Y, 0) are implicit.)"""
+    M = What.shape[0]
+    K = np.exp(tau * What)
+    # first iteration starts from X = tau*What with Q = 0 (no clip yet)
+    a = N / K.sum(1)
+    E = K * a[:, None]
+    b = N / E.sum(0)
+    P = E * b[None, :]
+    U = np.ones(M)
+    V = np.ones(M)
+    for _ in range(T - 1):
+        E = np.minimum(P * U[:, None] * V[None, :], 1.0)
+        a = N / E.sum(1)
+        b = N / (E * a[:, None]).sum(0)
+        U *= a
+        V *= b
+    return np.minimum(P * U[:, None] * V[None, :], 1.0)
+
+
+@pytest.mark.parametrize("M,N,tau,T", [(4, 2, 20.0, 50), (8, 4, 20.0, 100), (16, 8, 30.0, 40),
+                                       (32, 16, 40.0, 30), (8, 3, 10.0, 25)])
+def test_scaling_form_agrees(M, N, tau, T):
+    W = _block_matrix(7, M, nb=3, kind="student_t")
+    S64, _ = oracle.dykstra(W, N, M, tau, T)
+    Wh = _scores(W, M)
+    for bj in range(3):
+        ref = _scaling_form(Wh[0, bj], N, tau, T)
+        assert np.abs(S64[:, bj * M:(bj + 1) * M] - ref).max() < 1e-11
+
+
+def _dual_projection(What, N, tau):
+    """argmin KL(S || exp(tau*What)) s.t. S 1 = N, S^T 1 = N, 0 <= S <= 1, via
+    its dual: maximise sum_i N a_i + sum_j N b_j - sum_ij h(tau*What_ij + a_i + b_j)
+    with h(y) = e^y (y <= 0), 1 + y (y > 0);  S* = h'(y) = min(e^y, 1)."""
+    M = What.shape[0]
+    C = tau * What
+
+    def f(z):
+        a, b = z[:M], z[M:]
+        y = C + a[:, None] + b[None, :]
+        h = np.where(y <= 0, np.exp(np.minimum(y, 0)), 1 + y)
+        g = np.minimum(np.exp(np.minimum(y, 50)), 1.0)
+        val = h.sum() - N * a.sum() - N * b.sum()
+        return val, np.concatenate([g.sum(1) - N, g.sum(0) - N])
+
+    z0 = np.concatenate([-C.max(1), np.zeros(M)])
+    res = minimize(f, z0, jac=True, method="L-BFGS-B",
+                   options={"maxiter": 20000, "gtol": 1e-13, "ftol": 1e-16})
+    a, b = res.x[:M], res.x[M:]
+    return np.minimum(np.exp(C + a[:, None] + b[None, :]), 1.0)
+
+
+@pytest.mark.parametrize("M,N,tau", [(4, 2, 5.0), (8, 4, 5.0), (8, 2, 8.0)])
+def test_limit_is_kl_projection(M, N, tau):
+    W = _block_matrix(8, M, nb=3)
+    S64, _ = oracle.dykstra(W, N, M, tau, 4000)
+    Wh = _scores(W, M)
+    clipped = 0
+    for bj in range(3):
+        ref = _dual_projection(Wh[0, bj], N, tau)
+        got = S64[:, bj * M:(bj + 1) * M]
+        assert np.abs(got - ref).max() < 2e-6
+        clipped += int((ref > 1 - 1e-9).sum())
+        assert np.allclose(got.sum(0), N, atol=1e-9) and np.allclose(got.sum(1), N, atol=1e-9)
+    assert clipped > 0  # the clip binds somewhere, so the correction term matters
+
+
+def test_nonfinite_input_rejected():
+    W = _block_matrix(9, 4)
+    W[1, 1] = np.nan
+    with pytest.raises(ValueError):
+        oracle.dykstra(W, 2, 4, 20.0, 5)

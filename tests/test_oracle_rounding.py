@@ -1,0 +1,149 @@
+"""Pins for the oracle's rounding: greedy (R1), local search (R2), fill (R3).
+
+Rule (pith.science review of TSENOR, "What carries the argument"): sort the
+fractional entries descending, accept greedily while the row and column
+budgets remain, then a local search that swaps in (i,j'), (i',j) and removes
+(i',j') when |W_ij'| + |W_i'j| - |W_i'j'| is positive; a feasibility fill
+finishes any block still short of N.  Pins:
+
+* hand-derived 4x4 cases (tests/golden/rounding_cases.json);
+* the tau = 0 closed form: all keys tie, index order gives the block
+  diagonal of N x N all-ones tiles;
+* the greedy equals the unique stable b-matching of the key order,
+  found by brute force over every 0/1 matrix with row/column sums <= N;
+* every applied move changes the objective by exactly its score, R2 moves
+  are strictly positive, R2 + R3 moves equal the greedy shortfall;
+* every output is feasible, and never beats the exact optimum.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_mask_search_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden():
+    with open(os.path.join(GOLDEN, "rounding_cases.json")) as f:
+        return json.load(f)
+
+
+def test_golden_greedy_and_moves():
+    g = _golden()
+    S = np.array(g["S"], np.float32)
+    for case in g["cases"]:
+        A = np.array(case["A"], np.float32)
+        Z, info, Zg, scores = oracle.round_block(S, A, g["N"], case["L"], trace=True)
+        assert np.array_equal(Zg, np.array(g["greedy"])), case["name"]
+        assert np.array_equal(Z, np.array(case["mask"])), case["name"]
+        assert list(info) == case["info"], case["name"]
+        assert np.array_equal(scores, np.array(case["scores"], np.float32)), case["name"]
+
+
+@pytest.mark.parametrize("M,N", [(4, 2), (8, 4), (16, 8), (32, 16), (8, 2)])
+def test_tau_zero_block_diagonal(M, N):
+    W = wl.random_blocks(3, 4, M, "normal")
+    mask, S64, S32, stats = oracle.tsenor(W, N, M, 0.0, 5, 4)
+    Z = oracle.unpack_mask(mask, W.shape[1])
+    ref = np.zeros((M, M), bool)
+    for k in range(M // N):
+        ref[k * N:(k + 1) * N, k * N:(k + 1) * N] = True
+    for bj in range(4):
+        assert np.array_equal(Z[:, bj * M:(bj + 1) * M], ref)
+    assert stats[0] == 0
+
+
+def _key_order(S):
+    n = S.size
+    return sorted(range(n), key=lambda k: (-S.flat[k], k))
+
+
+def _stable_sets(S, N):
+    """All 0/1 matrices G with row/col sums <= N such that every entry outside
+    G has N entries of G ranked above it in its row or in its column."""
+    M = S.shape[0]
+    order = _key_order(S)
+    rank = np.empty(M * M, int)
+    rank[order] = np.arange(M * M)
+    rank = rank.reshape(M, M)
+    out = []
+    for bits in itertools.product((0, 1), repeat=M * M):
+        G = np.array(bits, bool).reshape(M, M)
+        if (G.sum(1) > N).any() or (G.sum(0) > N).any():
+            continue
+        ok = True
+        for i in range(M):
+            for j in range(M):
+                if G[i, j]:
+                    continue
+                above_r = (G[i] & (rank[i] < rank[i, j])).sum()
+                above_c = (G[:, j] & (rank[:, j] < rank[i, j])).sum()
+                if above_r < N and above_c < N:
+                    ok = False
+                    break
+            if not ok:
+                break
+        if ok:
+            out.append(G)
+    return out
+
+
+@pytest.mark.parametrize("M,N,seed", [(3, 1, 0), (3, 2, 1), (4, 1, 2), (4, 2, 3), (4, 2, 4),
+                                      (4, 3, 5)])
+def test_greedy_is_unique_stable_matching(M, N, seed):
+    rng = np.random.default_rng(seed)
+    for trial in range(2 if M == 4 else 6):
+        # coarse values -> many ties, broken by index
+        S = rng.choice(np.array([0.1, 0.3, 0.5, 1.0], np.float32), (M, M))
+        A = np.ones((M, M), np.float32)
+        _, _, Zg, _ = oracle.round_block(S, A, N, 0, trace=True)
+        stable = _stable_sets(S, N)
+        assert len(stable) == 1
+        assert np.array_equal(stable[0], Zg.astype(bool))
+
+
+@pytest.mark.parametrize("M,N,L", [(4, 2, 4), (8, 4, 8), (16, 8, 16), (32, 16, 32), (8, 3, 2),
+                                   (16, 8, 0)])
+def test_moves_feasibility_and_scores(M, N, L):
+    rng = np.random.default_rng(M * 100 + N * 10 + L)
+    seen_moves = 0
+    for trial in range(60):
+        A = np.abs(rng.standard_t(3, (M, M))).astype(np.float32)
+        # S: a noisy, partly clipped fractional matrix
+        S = np.clip(rng.uniform(0, 1.3, (M, M)), 0, 1).astype(np.float32)
+        Z, info, Zg, scores = oracle.round_block(S, A, N, L, trace=True)
+        assert np.all(Z.sum(0) == N) and np.all(Z.sum(1) == N)
+        D, n2, n3 = info
+        assert Zg.sum() == N * M - D and n2 + n3 == D and n2 <= L
+        assert np.all(scores[:n2] > 0)
+        gain = (Z.astype(np.float64) * A).sum() - (Zg.astype(np.float64) * A).sum()
+        assert gain == pytest.approx(float(np.sum(scores.astype(np.float64))), abs=1e-4)
+        opt, _ = oracle.exact_opt_block(A, N)
+        assert (Z.astype(np.float64) * A).sum() <= opt + 1e-9
+        seen_moves += D
+    assert seen_moves > 0
+
+
+def test_round_matrix_layout_and_feasible():
+    M, N = 8, 4
+    W = wl.random_blocks(12, 4, M, "student_t")
+    W = np.concatenate([W, wl.random_blocks(13, 4, M, "normal")], 0)  # 16 x 32
+    rng = np.random.default_rng(1)
+    S = rng.uniform(0, 1, W.shape).astype(np.float32)
+    mask, stats = oracle.round_matrix(S, W, N, M, 8)
+    Zfull = oracle.unpack_mask(mask, W.shape[1])
+    for bi in range(W.shape[0] // M):
+        for bj in range(W.shape[1] // M):
+            Zb = Zfull[bi * M:(bi + 1) * M, bj * M:(bj + 1) * M]
+            Zr, _ = oracle.round_block(S[bi * M:(bi + 1) * M, bj * M:(bj + 1) * M],
+                                       np.abs(W[bi * M:(bi + 1) * M, bj * M:(bj + 1) * M]), N, 8)
+            assert np.array_equal(Zb, Zr.astype(bool))
+    # bit layout: LSB of word 0 is column 0
+    w = np.zeros((1, 1), np.uint32)
+    w[0, 0] = 0b101
+    assert list(oracle.unpack_mask(w, 4)[0]) == [True, False, True, False]
