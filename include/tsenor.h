@@ -1,0 +1,129 @@
+/*
+ * tsenor.h -- C ABI of the MI355X (gfx950) transposable N:M mask-search library.
+ *
+ * What it computes (pith.science review of "TSENOR: Highly-Efficient Algorithm
+ * for Finding Transposable N:M Sparse Masks", arXiv 2505.23949, sections
+ * "What carries the argument" and "Core claim"):
+ *
+ *   The weight matrix W is tiled into aligned M x M blocks.  Each block gets a
+ *   0/1 mask with exactly N ones in every row and every column (so W and W^T are
+ *   both N:M sparse), chosen to keep as much of |W| as possible:
+ *     1. scores What = |W| / max_block |W|  (an all-zero block scores 0);
+ *     2. the block LP is solved as capacitated optimal transport with entropy
+ *        regularisation: start X = tau * What, Q = 0, then `iters` times
+ *        C1 row normalisation (rows of exp(X) sum to N),
+ *        C2 column normalisation (columns sum to N),
+ *        C3 clip at 1 with its Dykstra correction (Y = X+Q, X = min(Y,0),
+ *        Q = Y - X); the fractional result is S = exp(X) in [0,1];
+ *     3. rounding: order the entries by (S descending, in-block index i*M+j
+ *        ascending) and accept an entry while its row and column both hold
+ *        fewer than N ones; then up to `ls_steps` local-search moves, each the
+ *        best move over deficient row i, deficient column j and a kept
+ *        (i',j') with Z_ij' = Z_i'j = 0, scored in fp32 as
+ *        (|W_ij'| + |W_i'j|) - |W_i'j'|, ties to the smallest (i,j,i',j'),
+ *        applied only when the score is > 0; finally a feasibility fill that
+ *        repeats the same move (first deficient row and column, best (i',j'),
+ *        ties to the smallest) with no sign condition until every row and
+ *        column holds N ones.
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     never frees them and keeps no reference after the call.
+ *   - W is row-major: element (r, c) is at W[r * ld + c]; ld >= cols.
+ *     dtype TSENOR_F32 is IEEE fp32, TSENOR_BF16 is bfloat16 (raw 16-bit
+ *     patterns); all arithmetic is fp32 (bf16 widens exactly).
+ *   - The mask is bit-packed row-major into uint32 words: ceil(cols/32) words
+ *     per row, column c is bit (c % 32) of word (c / 32) (LSB = lowest column).
+ *     Bits beyond `cols` in a row's last word are written as 0.
+ *   - frac_out / S are fp32 [rows][cols] (leading dimension cols, resp. lds).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream); results are valid after the caller synchronises that stream.
+ *   - Argument errors are detected on the host before any HIP call: the call
+ *     returns the status and enqueues nothing.  Launch/runtime failures return
+ *     TSENOR_ERR_HIP; tsenor_last_error() then gives the HIP message.
+ *   - Results are deterministic: the same inputs give bit-identical masks and
+ *     S on every run and for every stream.  Non-finite weights give undefined
+ *     (but memory-safe) results.
+ *   - The library keeps one cached device workspace per device (allocated on
+ *     first use, grown on demand, never freed before process exit).  Calls on
+ *     one device share it: each launch is ordered after the previous one on
+ *     the device (stream event), so concurrent calls from any thread or
+ *     stream are safe but do not overlap.  The host side is thread-safe.
+ */
+#ifndef TSENOR_H
+#define TSENOR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TSENOR_F32 = 0, TSENOR_BF16 = 1 } tsenor_dtype;
+
+typedef enum {
+    TSENOR_OK = 0,
+    TSENOR_ERR_NULL = 1,  /* a required pointer is NULL                                */
+    TSENOR_ERR_SHAPE = 2, /* rows/cols <= 0, rows % M, cols % M, ld < cols, lds < cols   */
+    TSENOR_ERR_NM = 3,    /* M not in {4, 8, 16, 32}, or N < 1, or N > M                 */
+    TSENOR_ERR_PARAM = 4, /* tau not finite or < 0, iters < 1, ls_steps < 0, count < 0   */
+    TSENOR_ERR_DTYPE = 5, /* dtype not a tsenor_dtype                                   */
+    TSENOR_ERR_HIP = 6    /* HIP runtime or launch failure                              */
+} tsenor_status;
+
+/* Whole method (steps 1-3 above) on one matrix.
+ *   W        device, [rows][ld] of dtype; read only.
+ *   N, M     pattern: N ones per row and column of every M x M block.
+ *   tau      entropy strength (> = 0, finite), applied to block-max-normalised |W|.
+ *   iters    Dykstra cycles (C1, C2, C3), >= 1; no convergence test.
+ *   ls_steps maximum local-search moves per block, >= 0.
+ *   mask_out device, [rows][ceil(cols/32)] uint32, written entirely.
+ *   frac_out device, [rows][cols] fp32 fractional S, or NULL to skip.
+ *   stream   hipStream_t or NULL.                                              */
+int tsenor_mask(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,
+                float tau, int iters, int ls_steps, uint32_t* mask_out, float* frac_out,
+                void* stream);
+
+/* One matrix of a batch.  Field meanings as in tsenor_mask.                    */
+typedef struct {
+    const void* W;
+    int dtype;
+    int64_t rows, cols, ld;
+    int N, M;
+    uint32_t* mask_out;
+    float* frac_out; /* NULL = don't write */
+} tsenor_matrix;
+
+/* Many matrices (possibly of different shape, dtype and N:M) in one kernel
+ * launch, e.g. every projection of a transformer.  `mats` is a HOST array of
+ * `count` descriptors (count >= 0; 0 is a no-op); every descriptor is
+ * validated as in tsenor_mask before anything is enqueued.  tau, iters and
+ * ls_steps apply to all matrices.  The descriptor table is copied to the
+ * device on `stream` before the call returns, so `mats` may be reused
+ * immediately.                                                               */
+int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int iters,
+                        int ls_steps, void* stream);
+
+/* Rounding only (step 3) on a caller-supplied fractional matrix S.
+ *   S        device, [rows][lds] fp32, values in [0, 1] (as produced by the
+ *            solver; values outside [0,1] give an unspecified order), read only.
+ *   W        device, [rows][ld] of dtype; |W| scores the local-search moves.
+ * Other arguments as in tsenor_mask.                                           */
+int tsenor_round(const float* S, int64_t lds, const void* W, int dtype, int64_t rows,
+                 int64_t cols, int64_t ld, int N, int M, int ls_steps, uint32_t* mask_out,
+                 void* stream);
+
+/* Static, human-readable name of a status code (never NULL).                   */
+const char* tsenor_status_str(int status);
+
+/* Message of the last TSENOR_ERR_HIP on the calling thread ("" if none).       */
+const char* tsenor_last_error(void);
+
+/* ABI version: 0x00MMmmpp.                                                     */
+int tsenor_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSENOR_H */

@@ -1,0 +1,165 @@
+"""ctypes binding of libtsenor.so: the same entry points as include/tsenor.h."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "libtsenor.so")
+
+F32, BF16 = 0, 1
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+
+class TsenorError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        l = lib()
+        msg = l.tsenor_status_str(status).decode()
+        if status == 6:
+            msg += ": " + l.tsenor_last_error().decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+class _Matrix(ctypes.Structure):
+    _fields_ = [("W", _P), ("dtype", _I), ("rows", _I64), ("cols", _I64), ("ld", _I64),
+                ("N", _I), ("M", _I), ("mask_out", _P), ("frac_out", _P)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libtsenor.so (raises if it has not been built: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing; build it with `python -m sparse_mask_search_amd.build`")
+        l = ctypes.CDLL(_LIB_PATH)
+        l.tsenor_mask.argtypes = [_P, _I, _I64, _I64, _I64, _I, _I, _F, _I, _I, _P, _P, _P]
+        l.tsenor_mask.restype = _I
+        l.tsenor_round.argtypes = [_P, _I64, _P, _I, _I64, _I64, _I64, _I, _I, _I, _P, _P]
+        l.tsenor_round.restype = _I
+        l.tsenor_mask_batched.argtypes = [ctypes.POINTER(_Matrix), _I, _F, _I, _I, _P]
+        l.tsenor_mask_batched.restype = _I
+        l.tsenor_status_str.argtypes = [_I]
+        l.tsenor_status_str.restype = ctypes.c_char_p
+        l.tsenor_last_error.argtypes = []
+        l.tsenor_last_error.restype = ctypes.c_char_p
+        l.tsenor_version.restype = _I
+        _lib = l
+    return _lib
+
+
+def version() -> int:
+    return int(lib().tsenor_version())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _weights(W):
+    torch = _torch()
+    if not isinstance(W, torch.Tensor) or not W.is_cuda:
+        raise TypeError("W must be a CUDA (HIP) torch tensor")
+    if W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be 2-D with unit column stride")
+    if W.dtype == torch.float32:
+        return F32
+    if W.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("W must be float32 or bfloat16")
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _mask_buffer(W):
+    torch = _torch()
+    rows, cols = W.shape
+    return torch.empty((rows, (cols + 31) // 32), dtype=torch.int32, device=W.device)
+
+
+def mask(W, N: int, M: int, tau: float, iters: int, ls_steps: int, return_frac: bool = False,
+         out=None, frac_out=None, stream=None):
+    """Transposable N:M mask of W (fp32 or bf16 CUDA tensor).
+
+    Returns (mask, frac): mask is int32 [rows, ceil(cols/32)] holding the
+    uint32 bit words (bit c%32 of word c/32 = column c); frac is the fp32
+    fractional solution S [rows, cols] if requested, else None."""
+    torch = _torch()
+    dt = _weights(W)
+    rows, cols = W.shape
+    out = _mask_buffer(W) if out is None else out
+    if frac_out is None and return_frac:
+        frac_out = torch.empty((rows, cols), dtype=torch.float32, device=W.device)
+    st = lib().tsenor_mask(ctypes.c_void_p(W.data_ptr()), dt, rows, cols, W.stride(0), N, M,
+                           float(tau), int(iters), int(ls_steps), ctypes.c_void_p(out.data_ptr()),
+                           ctypes.c_void_p(frac_out.data_ptr() if frac_out is not None else 0),
+                           _stream(stream))
+    if st != 0:
+        raise TsenorError(st, "tsenor_mask")
+    return out, frac_out
+
+
+def round_mask(S, W, N: int, M: int, ls_steps: int, out=None, stream=None):
+    """Rounding only (greedy, local search, fill) of a fractional S [rows, cols]."""
+    torch = _torch()
+    dt = _weights(W)
+    if S.dtype != torch.float32 or not S.is_cuda or S.dim() != 2 or S.stride(1) != 1:
+        raise TypeError("S must be a 2-D float32 CUDA tensor with unit column stride")
+    if tuple(S.shape) != tuple(W.shape):
+        raise ValueError("S and W shapes differ")
+    rows, cols = W.shape
+    out = _mask_buffer(W) if out is None else out
+    st = lib().tsenor_round(ctypes.c_void_p(S.data_ptr()), S.stride(0),
+                            ctypes.c_void_p(W.data_ptr()), dt, rows, cols, W.stride(0), N, M,
+                            int(ls_steps), ctypes.c_void_p(out.data_ptr()), _stream(stream))
+    if st != 0:
+        raise TsenorError(st, "tsenor_round")
+    return out
+
+
+def mask_batched(items, tau: float, iters: int, ls_steps: int, return_frac: bool = False,
+                 stream=None):
+    """One launch over many matrices.  items: iterable of (W, N, M).
+    Returns a list of (mask, frac_or_None) in the same order."""
+    torch = _torch()
+    items = list(items)
+    arr = (_Matrix * max(1, len(items)))()
+    outs = []
+    for k, (W, N, M) in enumerate(items):
+        dt = _weights(W)
+        rows, cols = W.shape
+        m = _mask_buffer(W)
+        f = torch.empty((rows, cols), dtype=torch.float32, device=W.device) if return_frac else None
+        arr[k] = _Matrix(W.data_ptr(), dt, rows, cols, W.stride(0), N, M, m.data_ptr(),
+                         f.data_ptr() if f is not None else 0)
+        outs.append((m, f))
+    st = lib().tsenor_mask_batched(arr, len(items), float(tau), int(iters), int(ls_steps),
+                                   _stream(stream))
+    if st != 0:
+        raise TsenorError(st, "tsenor_mask_batched")
+    return outs
+
+
+def unpack(mask_words, cols: int):
+    """int32/uint32 words [rows, ceil(cols/32)] -> bool [rows, cols] (same device)."""
+    torch = _torch()
+    w = mask_words.to(torch.int64) & 0xFFFFFFFF
+    bits = (w.unsqueeze(-1) >> torch.arange(32, device=w.device)) & 1
+    return bits.reshape(w.shape[0], -1)[:, :cols].bool()

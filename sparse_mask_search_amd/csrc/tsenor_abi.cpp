@@ -1,0 +1,288 @@
+// tsenor_abi.cpp -- the extern "C" boundary declared in include/tsenor.h.
+//
+// Host-side only: argument validation (before any HIP call), the per-device
+// workspace cache, launch geometry, and the stream ordering that makes the
+// shared workspace safe.  The arithmetic of the method lives entirely in the
+// kernels (tsenor_kernels.hip).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "tsenor.h"
+#include "tsenor_internal.h"
+
+using tsenor::MatJob;
+using tsenor::Params;
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char* where) {
+    std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", where, hipGetErrorString(e));
+    return TSENOR_ERR_HIP;
+}
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+    std::mutex mu;
+    bool init = false;
+    int num_cu = 0;
+    float* scratch = nullptr;
+    size_t scratch_slots = 0;
+    hipEvent_t last = nullptr;      // completion of the newest launch that used this state
+    MatJob* jobs_dev = nullptr;     // batched descriptor table (device)
+    MatJob* jobs_host = nullptr;    // pinned staging copy
+    size_t jobs_cap = 0;
+    int occ_mask[2][33] = {};
+    int occ_round[2][33] = {};
+    int occ_batched = 0;
+};
+DeviceState g_dev[kMaxDevices];
+
+bool valid_m(int M) { return M == 4 || M == 8 || M == 16 || M == 32; }
+
+int check_matrix(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,
+                 const void* mask) {
+    if (W == nullptr || mask == nullptr) return TSENOR_ERR_NULL;
+    if (dtype != TSENOR_F32 && dtype != TSENOR_BF16) return TSENOR_ERR_DTYPE;
+    if (!valid_m(M) || N < 1 || N > M) return TSENOR_ERR_NM;
+    if (rows <= 0 || cols <= 0 || rows % M != 0 || cols % M != 0 || ld < cols)
+        return TSENOR_ERR_SHAPE;
+    // keep every element offset inside int64 comfortably
+    if (rows > (int64_t(1) << 40) / ld) return TSENOR_ERR_SHAPE;
+    return TSENOR_OK;
+}
+
+int check_params(float tau, int iters, int ls_steps) {
+    if (!std::isfinite(tau) || tau < 0.0f || iters < 1 || ls_steps < 0) return TSENOR_ERR_PARAM;
+    return TSENOR_OK;
+}
+
+MatJob make_job(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,
+                uint32_t* mask, float* frac) {
+    MatJob j;
+    j.W = W;
+    j.mask = mask;
+    j.frac = frac;
+    j.rows = rows;
+    j.cols = cols;
+    j.ld = ld;
+    j.wpr = (cols + 31) / 32;
+    j.group_begin = 0;
+    j.N = N;
+    j.M = M;
+    j.bf16 = dtype == TSENOR_BF16 ? 1 : 0;
+    const int64_t es = j.bf16 ? 2 : 4;
+    j.aligned = ((reinterpret_cast<uintptr_t>(W) & 15u) == 0 && (ld * es) % 16 == 0) ? 1 : 0;
+    return j;
+}
+
+int64_t groups_of(const MatJob& j) {
+    const int64_t bpg = tsenor::blocks_per_group(j.M);
+    const int64_t nbc = j.cols / j.M;
+    return (j.rows / j.M) * ((nbc + bpg - 1) / bpg);
+}
+
+// Lock, initialise and return the current device's state.
+int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return hip_fail(hipErrorInvalidDevice, "device index");
+    DeviceState& st = g_dev[dev];
+    *lk = std::unique_lock<std::mutex>(st.mu);
+    if (!st.init) {
+        e = hipDeviceGetAttribute(&st.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+        e = hipEventCreateWithFlags(&st.last, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        for (int b = 0; b < 2; ++b)
+            for (int M : {4, 8, 16, 32}) {
+                st.occ_mask[b][M] = tsenor::occupancy_mask(M, b);
+                st.occ_round[b][M] = tsenor::occupancy_round(M, b);
+            }
+        st.occ_batched = tsenor::occupancy_batched();
+        st.init = true;
+    }
+    *out = &st;
+    return TSENOR_OK;
+}
+
+// Ensure `slots` workspace slots exist.  Growing waits for every earlier
+// launch that may still read the old buffer.
+int ensure_scratch(DeviceState& st, size_t slots) {
+    if (st.scratch_slots >= slots) return TSENOR_OK;
+    hipError_t e;
+    if (st.scratch != nullptr) {
+        e = hipEventSynchronize(st.last);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        e = hipFree(st.scratch);
+        if (e != hipSuccess) return hip_fail(e, "hipFree");
+        st.scratch = nullptr;
+        st.scratch_slots = 0;
+    }
+    e = hipMalloc(&st.scratch, slots * tsenor::kSlotFloats * sizeof(float));
+    if (e != hipSuccess) {
+        st.scratch = nullptr;
+        return hip_fail(e, "hipMalloc(workspace)");
+    }
+    st.scratch_slots = slots;
+    return TSENOR_OK;
+}
+
+int64_t clamp_grid(int64_t groups, int num_cu, int occ) {
+    int64_t cap = (int64_t)num_cu * (occ > 0 ? occ : 1);
+    return groups < cap ? groups : cap;
+}
+
+int order_and_record_begin(DeviceState& st, hipStream_t s) {
+    hipError_t e = hipStreamWaitEvent(s, st.last, 0);
+    return e == hipSuccess ? TSENOR_OK : hip_fail(e, "hipStreamWaitEvent");
+}
+
+int record_end(DeviceState& st, hipStream_t s) {
+    hipError_t e = hipEventRecord(st.last, s);
+    return e == hipSuccess ? TSENOR_OK : hip_fail(e, "hipEventRecord");
+}
+
+}  // namespace
+
+extern "C" {
+
+int tsenor_mask(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,
+                float tau, int iters, int ls_steps, uint32_t* mask_out, float* frac_out,
+                void* stream) {
+    int st_code = check_matrix(W, dtype, rows, cols, ld, N, M, mask_out);
+    if (st_code != TSENOR_OK) return st_code;
+    st_code = check_params(tau, iters, ls_steps);
+    if (st_code != TSENOR_OK) return st_code;
+
+    DeviceState* st = nullptr;
+    std::unique_lock<std::mutex> lk;
+    if ((st_code = acquire(&st, &lk)) != TSENOR_OK) return st_code;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, frac_out);
+    const int64_t grid = clamp_grid(groups_of(job), st->num_cu, st->occ_mask[job.bf16][M]);
+    if ((st_code = ensure_scratch(*st, (size_t)grid)) != TSENOR_OK) return st_code;
+    Params prm;
+    prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
+    prm.iters = iters;
+    prm.ls_steps = ls_steps;
+    prm.scratch = st->scratch;
+    if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
+    hipError_t e = (hipError_t)tsenor::launch_mask(job, prm, (int)grid, stream);
+    if (e != hipSuccess) return hip_fail(e, "mask kernel launch");
+    return record_end(*st, s);
+}
+
+int tsenor_round(const float* S, int64_t lds, const void* W, int dtype, int64_t rows,
+                 int64_t cols, int64_t ld, int N, int M, int ls_steps, uint32_t* mask_out,
+                 void* stream) {
+    if (S == nullptr) return TSENOR_ERR_NULL;
+    int st_code = check_matrix(W, dtype, rows, cols, ld, N, M, mask_out);
+    if (st_code != TSENOR_OK) return st_code;
+    if (lds < cols) return TSENOR_ERR_SHAPE;
+    if (ls_steps < 0) return TSENOR_ERR_PARAM;
+
+    DeviceState* st = nullptr;
+    std::unique_lock<std::mutex> lk;
+    if ((st_code = acquire(&st, &lk)) != TSENOR_OK) return st_code;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, nullptr);
+    const int64_t per_pass = tsenor::kWave / M;
+    const int64_t nbc = cols / M;
+    const int64_t groups = (rows / M) * ((nbc + per_pass - 1) / per_pass);
+    const int64_t grid = clamp_grid(groups, st->num_cu, st->occ_round[job.bf16][M]);
+    if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
+    hipError_t e = (hipError_t)tsenor::launch_round(job, S, lds, ls_steps, (int)grid, stream);
+    if (e != hipSuccess) return hip_fail(e, "round kernel launch");
+    return record_end(*st, s);
+}
+
+int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int iters, int ls_steps,
+                        void* stream) {
+    if (count < 0) return TSENOR_ERR_PARAM;
+    if (count > 0 && mats == nullptr) return TSENOR_ERR_NULL;
+    int st_code = check_params(tau, iters, ls_steps);
+    if (st_code != TSENOR_OK) return st_code;
+    for (int i = 0; i < count; ++i) {
+        const tsenor_matrix& m = mats[i];
+        st_code = check_matrix(m.W, m.dtype, m.rows, m.cols, m.ld, m.N, m.M, m.mask_out);
+        if (st_code != TSENOR_OK) return st_code;
+    }
+    if (count == 0) return TSENOR_OK;
+
+    DeviceState* st = nullptr;
+    std::unique_lock<std::mutex> lk;
+    if ((st_code = acquire(&st, &lk)) != TSENOR_OK) return st_code;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (st->jobs_cap < (size_t)count) {
+        if (st->jobs_dev != nullptr) {
+            e = hipEventSynchronize(st->last);
+            if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+            (void)hipFree(st->jobs_dev);
+            (void)hipHostFree(st->jobs_host);
+            st->jobs_dev = nullptr;
+            st->jobs_host = nullptr;
+            st->jobs_cap = 0;
+        }
+        e = hipMalloc(&st->jobs_dev, sizeof(MatJob) * (size_t)count);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(descriptors)");
+        e = hipHostMalloc(reinterpret_cast<void**>(&st->jobs_host), sizeof(MatJob) * (size_t)count,
+                          hipHostMallocDefault);
+        if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(descriptors)");
+        st->jobs_cap = (size_t)count;
+    } else {
+        // the pinned staging copy may still be read by the previous upload
+        e = hipEventSynchronize(st->last);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    }
+    int64_t total = 0;
+    for (int i = 0; i < count; ++i) {
+        const tsenor_matrix& m = mats[i];
+        MatJob j = make_job(m.W, m.dtype, m.rows, m.cols, m.ld, m.N, m.M, m.mask_out, m.frac_out);
+        j.group_begin = total;
+        total += groups_of(j);
+        st->jobs_host[i] = j;
+    }
+    const int64_t grid = clamp_grid(total, st->num_cu, st->occ_batched);
+    if ((st_code = ensure_scratch(*st, (size_t)grid)) != TSENOR_OK) return st_code;
+    Params prm;
+    prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
+    prm.iters = iters;
+    prm.ls_steps = ls_steps;
+    prm.scratch = st->scratch;
+    if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
+    e = hipMemcpyAsync(st->jobs_dev, st->jobs_host, sizeof(MatJob) * (size_t)count,
+                       hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
+    e = (hipError_t)tsenor::launch_batched(st->jobs_dev, count, total, 32, prm, (int)grid, stream);
+    if (e != hipSuccess) return hip_fail(e, "batched kernel launch");
+    return record_end(*st, s);
+}
+
+const char* tsenor_status_str(int status) {
+    switch (status) {
+        case TSENOR_OK: return "ok";
+        case TSENOR_ERR_NULL: return "required pointer is NULL";
+        case TSENOR_ERR_SHAPE: return "bad shape (rows/cols must be positive multiples of M, ld >= cols)";
+        case TSENOR_ERR_NM: return "bad N:M (M in {4,8,16,32}, 1 <= N <= M)";
+        case TSENOR_ERR_PARAM: return "bad parameter (tau finite >= 0, iters >= 1, ls_steps >= 0)";
+        case TSENOR_ERR_DTYPE: return "bad dtype (TSENOR_F32 or TSENOR_BF16)";
+        case TSENOR_ERR_HIP: return "HIP runtime error (see tsenor_last_error)";
+        default: return "unknown status";
+    }
+}
+
+const char* tsenor_last_error(void) { return g_last_error; }
+
+int tsenor_version(void) { return 0x000100; }
+
+}  // extern "C"

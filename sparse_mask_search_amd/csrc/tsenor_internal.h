@@ -1,0 +1,48 @@
+// tsenor_internal.h -- shared between the host ABI layer and the HIP kernels.
+// Not installed; the public interface is include/tsenor.h.
+#pragma once
+#include <stdint.h>
+
+namespace tsenor {
+
+// One matrix as the kernels see it.
+struct MatJob {
+    const void* W;      // device, [rows][ld]
+    uint32_t* mask;     // device, [rows][wpr]
+    float* frac;        // device, [rows][cols] or nullptr
+    int64_t rows, cols, ld, wpr;
+    int64_t group_begin;  // first global group id of this matrix (batched launch)
+    int32_t N, M;
+    int32_t bf16;       // 1 = bfloat16 weights, 0 = fp32
+    int32_t aligned;    // 1 = W rows may be read with 16-byte vector loads
+};
+
+// Scalars shared by every matrix of a launch.
+struct Params {
+    float tau_log2e;    // tau * log2(e): the Gibbs exponent in base 2
+    int32_t iters;
+    int32_t ls_steps;
+    float* scratch;     // one slot of kSlotFloats per workgroup
+};
+
+// Work decomposition: one workgroup = one wave (64 lanes) processes a "group"
+// of horizontally adjacent blocks of one block-row; see blocks_per_group().
+constexpr int kWave = 64;
+constexpr int64_t kSlotFloats = 8192;  // 32 KiB: max over M of blocks_per_group * M * M
+
+// Blocks per group: M=32 -> 8 (8 lanes per block), M=16 -> 16 (4 lanes per
+// block), M=8 and M=4 -> 64 (one lane per block).
+inline int blocks_per_group(int M) { return M == 32 ? 8 : (M == 16 ? 16 : 64); }
+
+// Host-side launchers (tsenor_kernels.hip).  They return a hipError_t value.
+int launch_mask(const MatJob& job, const Params& prm, int grid, void* stream);
+int launch_round(const MatJob& job, const float* S, int64_t lds, int ls_steps, int grid,
+                 void* stream);
+int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int max_m,
+                   const Params& prm, int grid, void* stream);
+// Number of 64-lane workgroups of each kernel that fit on one CU at once.
+int occupancy_mask(int M, int bf16);
+int occupancy_round(int M, int bf16);
+int occupancy_batched();
+
+}  // namespace tsenor

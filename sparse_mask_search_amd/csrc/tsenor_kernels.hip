@@ -1,0 +1,839 @@
+// tsenor_kernels.hip -- gfx950 kernels for transposable N:M mask search.
+//
+// Method: pith.science review of "TSENOR: Highly-Efficient Algorithm for Finding
+// Transposable N:M Sparse Masks" (arXiv 2505.23949), "What carries the argument"
+// and "Core claim": entropic capacitated OT per M x M block solved by Dykstra's
+// projections (row normalisation C1, column normalisation C2, clip at 1 with its
+// correction C3), then rounding by a descending sort, greedy within row/column
+// budgets, swap local search and a feasibility fill.
+//
+// One 64-lane workgroup (one wave) owns a "group" of horizontally adjacent
+// blocks of one block-row and runs the whole path for them:
+//
+//  1. gather   each lane reads R full rows of its block straight from HBM
+//              (16-byte loads), |W| -> fp32, block max by lane shuffles.
+//  2. solve    first Dykstra cycle in log2 space (max-shifted log-sum-exp on
+//              rows and columns, robust for any tau); every later cycle in
+//              scaling form.  With Y = X + Q the cycle is Y += a_i + b_j and
+//              X = min(Y, 0), so keeping P = 2^Y (fixed after cycle 1), a row
+//              scale U_i = 1/rho_i and a column scale V_j, one cycle is
+//                 t_ij = min(P_ij V_j, rho_i)     (= exp(X_ij) * rho_i)
+//                 R_i  = sum_j t_ij,  U_i = N/R_i,  rho_i = R_i/N      (C1)
+//                 C_j  = sum_i t_ij U_i,  V_j *= N/C_j          (C2, C3 implicit)
+//              i.e. 4 fp32 VALU ops per element and no transcendental per
+//              element.  Rows live in lanes; column sums of blocks spread over
+//              several lanes are reduced through LDS (reduce-scatter, then a
+//              broadcast of the new V).
+//  3. export   S = min(P V U, 1) is written to the workgroup's scratch slot
+//              (and to frac_out when asked).
+//  4. round    blocks are re-read from the slot one row and one column per
+//              lane.  The greedy over the (S desc, index asc) order is computed
+//              as its equivalent fixed point: accepted = {key >= phi_i and
+//              key >= theta_j} where phi_i / theta_j is the N-th largest key
+//              of row i / column j among entries passing the other side's
+//              thresholds.  Alternating the two updates from "everything
+//              allowed" climbs monotonically to that unique fixed point (the
+//              stable b-matching of the key order), so each step is a
+//              per-lane walk over a register-sorted row or column plus a
+//              32x32 bit-matrix transpose by lane shuffles.
+//  5. repair   local search and fill on the few deficient rows/columns, each
+//              move an exact argmax over packed (fp32 score, index) keys.
+//  6. pack     row bit masks are OR-combined across the blocks of a word and
+//              stored as uint32 words.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tsenor_internal.h"
+
+namespace tsenor {
+namespace {
+
+// Rows per lane (R), lanes per block (L) and blocks per group (BPG) for the solve.
+template <int M> struct Geo;
+template <> struct Geo<4> { static constexpr int R = 4, L = 1, BPG = 64; };
+template <> struct Geo<8> { static constexpr int R = 8, L = 1, BPG = 64; };
+template <> struct Geo<16> { static constexpr int R = 4, L = 4, BPG = 16; };
+template <> struct Geo<32> { static constexpr int R = 4, L = 8, BPG = 8; };
+
+template <int M> constexpr int kPadRow = M + 4;                          // floats per lane row
+template <int M> constexpr int kBlkStride = Geo<M>::L * kPadRow<M>;     // floats per block
+template <int M> constexpr int kBcastOff = Geo<M>::BPG * kBlkStride<M>;  // start of V broadcast
+template <int M> constexpr int dyk_lds_floats() {
+    return Geo<M>::L == 1 ? 0 : kBcastOff<M> + Geo<M>::BPG * kPadRow<M>;
+}
+template <int M> constexpr int rnd_lds_floats() { return (kWave / M) * M * (M + 1) + kWave; }
+template <int M> constexpr int lds_floats() {
+    return dyk_lds_floats<M>() > rnd_lds_floats<M>() ? dyk_lds_floats<M>() : rnd_lds_floats<M>();
+}
+constexpr int kMaxLdsFloats = lds_floats<32>() > lds_floats<16>() ? lds_floats<32>() : lds_floats<16>();
+
+template <int M> constexpr uint32_t kFull = (M == 32) ? 0xFFFFFFFFu : ((1u << M) - 1u);
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcpf(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ---------------------------------------------------------------- gather
+// |W| of M consecutive elements starting at element offset `off`, as fp32.
+template <int M, bool BF16>
+__device__ __forceinline__ void load_abs_row(const void* W, int64_t off, bool vec, float (&out)[M]) {
+    if constexpr (BF16) {
+        const uint16_t* p = static_cast<const uint16_t*>(W) + off;
+        if (vec) {
+            if constexpr (M >= 8) {
+#pragma unroll
+                for (int q = 0; q < M / 8; ++q) {
+                    const uint4 v = reinterpret_cast<const uint4*>(p)[q];
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        out[8 * q + 2 * h] = __uint_as_float((w[h] & 0x7FFFu) << 16);
+                        out[8 * q + 2 * h + 1] = __uint_as_float(w[h] & 0x7FFF0000u);
+                    }
+                }
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(p);
+                out[0] = __uint_as_float((v.x & 0x7FFFu) << 16);
+                out[1] = __uint_as_float(v.x & 0x7FFF0000u);
+                out[2] = __uint_as_float((v.y & 0x7FFFu) << 16);
+                out[3] = __uint_as_float(v.y & 0x7FFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < M; ++j) out[j] = __uint_as_float((uint32_t)(p[j] & 0x7FFFu) << 16);
+        }
+    } else {
+        const float* p = static_cast<const float*>(W) + off;
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < M / 4; ++q) {
+                const float4 v = reinterpret_cast<const float4*>(p)[q];
+                out[4 * q] = fabsf(v.x);
+                out[4 * q + 1] = fabsf(v.y);
+                out[4 * q + 2] = fabsf(v.z);
+                out[4 * q + 3] = fabsf(v.w);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < M; ++j) out[j] = fabsf(p[j]);
+        }
+    }
+}
+
+// M consecutive fp32 values (16-byte loads when `vec`).
+template <int M>
+__device__ __forceinline__ void load_row_f32(const float* p, bool vec, float (&out)[M]) {
+    if (vec) {
+#pragma unroll
+        for (int q = 0; q < M / 4; ++q) {
+            const float4 v = reinterpret_cast<const float4*>(p)[q];
+            out[4 * q] = v.x; out[4 * q + 1] = v.y; out[4 * q + 2] = v.z; out[4 * q + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < M; ++j) out[j] = p[j];
+    }
+}
+
+template <int M>
+__device__ __forceinline__ float tree_sum(const float (&v)[M]) {
+    float s[M / 2];
+#pragma unroll
+    for (int j = 0; j < M / 2; ++j) s[j] = v[2 * j] + v[2 * j + 1];
+#pragma unroll
+    for (int w = M / 4; w >= 1; w >>= 1) {
+#pragma unroll
+        for (int j = 0; j < w; ++j) s[j] = s[2 * j] + s[2 * j + 1];
+    }
+    return s[0];
+}
+
+// Column totals of a block whose rows are spread over L lanes: every lane
+// writes its M partials, lane k of the block adds up columns [4k, 4k+4) and
+// stores them to the block's broadcast row, which every lane then reads.
+// With kind == 0 the totals are broadcast as they are (combine = max or sum);
+// kind == 1 turns each total C_j into V_j * N / C_j, V_j being the value
+// currently in the broadcast row (so V never needs dynamic register indexing).
+// Returns, for kind == 1, whether any of this lane's four new V_j left
+// [2^-40, 2^40].
+template <int M, int KIND, bool MAXOP>
+__device__ __forceinline__ bool col_exchange(const float (&part)[M], float (&out)[M], float* lds,
+                                             int blk, int k, float fN) {
+    constexpr int L = Geo<M>::L;
+    static_assert(M / L == 4, "one float4 of columns per lane");
+    float* mine = lds + blk * kBlkStride<M> + k * kPadRow<M>;
+#pragma unroll
+    for (int q = 0; q < M / 4; ++q)
+        *reinterpret_cast<float4*>(mine + 4 * q) =
+            make_float4(part[4 * q], part[4 * q + 1], part[4 * q + 2], part[4 * q + 3]);
+    __syncthreads();
+    const float* base = lds + blk * kBlkStride<M> + 4 * k;
+    float4 acc = *reinterpret_cast<const float4*>(base);
+#pragma unroll
+    for (int kk = 1; kk < L; ++kk) {
+        const float4 v = *reinterpret_cast<const float4*>(base + kk * kPadRow<M>);
+        if constexpr (MAXOP) {
+            acc.x = fmaxf(acc.x, v.x); acc.y = fmaxf(acc.y, v.y);
+            acc.z = fmaxf(acc.z, v.z); acc.w = fmaxf(acc.w, v.w);
+        } else {
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+    }
+    float* bc = lds + kBcastOff<M> + blk * kPadRow<M>;
+    bool bad = false;
+    if constexpr (KIND == 1) {
+        const float4 vo = *reinterpret_cast<const float4*>(bc + 4 * k);
+        acc.x = vo.x * (fN * rcpf(acc.x));
+        acc.y = vo.y * (fN * rcpf(acc.y));
+        acc.z = vo.z * (fN * rcpf(acc.z));
+        acc.w = vo.w * (fN * rcpf(acc.w));
+        const float lo = fminf(fminf(acc.x, acc.y), fminf(acc.z, acc.w));
+        const float hi = fmaxf(fmaxf(acc.x, acc.y), fmaxf(acc.z, acc.w));
+        bad = !(lo >= 0x1p-40f && hi <= 0x1p40f);
+    }
+    *reinterpret_cast<float4*>(bc + 4 * k) = acc;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < M / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(bc + 4 * q);
+        out[4 * q] = v.x; out[4 * q + 1] = v.y; out[4 * q + 2] = v.z; out[4 * q + 3] = v.w;
+    }
+    return bad;
+}
+
+// ---------------------------------------------------------------- solve
+// Dykstra for the group's blocks; writes S (fp32) for block b of the group to
+// slot[b*M*M ...] row-major, and to job.frac when requested.
+template <int M, bool BF16>
+__device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& prm, int64_t br,
+                                              int64_t bc0, float* __restrict__ slot,
+                                              float* __restrict__ lds) {
+    constexpr int R = Geo<M>::R, L = Geo<M>::L;
+    const int lane = threadIdx.x;
+    const int blk = lane / L, k = lane % L;
+    const int64_t nbc = job.cols / M;
+    const int64_t bc = bc0 + blk;
+    const bool valid = bc < nbc;
+    const float fN = (float)job.N;
+    const float invN = 1.0f / fN;
+    const float log2N = log2f(fN);
+    const bool vec = job.aligned != 0;
+
+    float P[R][M];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (valid) {
+            load_abs_row<M, BF16>(job.W, (br * M + k * R + r) * job.ld + bc * M, vec, P[r]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < M; ++j) P[r][j] = 0.f;
+        }
+    }
+    // scores What = A / max(A); X = tau * What in log2 units
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < M; ++j) m = fmaxf(m, P[r][j]);
+#pragma unroll
+    for (int s = 1; s < L; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
+    const float scale = (m > 0.f) ? prm.tau_log2e / m : 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int j = 0; j < M; ++j) P[r][j] *= scale;
+
+    // ---- cycle 1 in log2 space (Q = 0, so no clip enters C1/C2) ----
+#pragma unroll
+    for (int r = 0; r < R; ++r) {  // C1
+        float mx = P[r][0];
+#pragma unroll
+        for (int j = 1; j < M; ++j) mx = fmaxf(mx, P[r][j]);
+        float e[M];
+#pragma unroll
+        for (int j = 0; j < M; ++j) e[j] = ex2(P[r][j] - mx);
+        const float a = log2N - mx - lg2(tree_sum<M>(e));
+#pragma unroll
+        for (int j = 0; j < M; ++j) P[r][j] += a;
+    }
+    {  // C2: column max, then column sum of 2^(x - max)
+        float part[M], cmax[M], csum[M];
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            float v = P[0][j];
+#pragma unroll
+            for (int r = 1; r < R; ++r) v = fmaxf(v, P[r][j]);
+            part[j] = v;
+        }
+        if constexpr (L == 1) {
+#pragma unroll
+            for (int j = 0; j < M; ++j) cmax[j] = part[j];
+        } else {
+            col_exchange<M, 0, true>(part, cmax, lds, blk, k, fN);
+        }
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            float v = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) v += ex2(P[r][j] - cmax[j]);
+            part[j] = v;
+        }
+        if constexpr (L == 1) {
+#pragma unroll
+            for (int j = 0; j < M; ++j) csum[j] = part[j];
+        } else {
+            col_exchange<M, 0, false>(part, csum, lds, blk, k, fN);
+        }
+        // C3 of cycle 1 is carried by P = 2^Y: X = min(Y, 0) appears as min(P V U, 1)
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            const float b = log2N - cmax[j] - lg2(csum[j]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) P[r][j] = ex2(P[r][j] + b);
+        }
+    }
+
+    // ---- cycles 2..T in scaling form ----
+    float V[M], rho[R];
+#pragma unroll
+    for (int j = 0; j < M; ++j) V[j] = 1.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) rho[r] = 1.f;
+    if constexpr (L > 1) {
+        float* bcr = lds + kBcastOff<M> + blk * kPadRow<M>;
+        *reinterpret_cast<float4*>(bcr + 4 * k) = make_float4(1.f, 1.f, 1.f, 1.f);
+        // made visible by the first exchange's barrier
+    }
+    for (int it = 1; it < prm.iters; ++it) {
+        float cacc[M];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float t[M], acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < M; ++j) {
+                t[j] = fminf(P[r][j] * V[j], rho[r]);
+                acc[j & 3] += t[j];
+            }
+            const float rs = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            const float u = fN * rcpf(rs);
+            rho[r] = rs * invN;
+#pragma unroll
+            for (int j = 0; j < M; ++j) cacc[j] = (r == 0) ? t[j] * u : fmaf(t[j], u, cacc[j]);
+        }
+        // Scale guard.  After cycle 1 every row/column factor lies in
+        // [1/M, M], so checking every 4th cycle against 2^+-40 keeps P V U,
+        // rho and V far inside the fp32 range.
+        bool bad = false;
+        if constexpr (L == 1) {
+#pragma unroll
+            for (int j = 0; j < M; ++j) V[j] = V[j] * (fN * rcpf(cacc[j]));
+            if ((it & 3) == 0) {
+                float lo = V[0], hi = V[0];
+#pragma unroll
+                for (int j = 1; j < M; ++j) { lo = fminf(lo, V[j]); hi = fmaxf(hi, V[j]); }
+                bad = !(lo >= 0x1p-40f && hi <= 0x1p40f);
+            }
+        } else {
+            bad = col_exchange<M, 1, false>(cacc, V, lds, blk, k, fN);
+        }
+        if ((it & 3) != 0) continue;
+#pragma unroll
+        for (int r = 0; r < R; ++r) bad |= !(rho[r] >= 0x1p-40f && rho[r] <= 0x1p40f);
+        bad = bad && valid;
+        if (__builtin_expect(__ballot(bad) != 0ull, 0)) {
+            // Rare: fold the scales into P (P <- P V U, scales <- 1) so that
+            // they stay far from the fp32 range limits.  Z = P U V is unchanged.
+            int f = bad ? 1 : 0;
+#pragma unroll
+            for (int s = 1; s < L; s <<= 1) f |= __shfl_xor(f, s);
+            if (f) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float u = fN * rcpf(rho[r] * fN);
+#pragma unroll
+                    for (int j = 0; j < M; ++j) P[r][j] = (P[r][j] * V[j]) * u;
+                }
+#pragma unroll
+                for (int j = 0; j < M; ++j) V[j] = 1.f;
+#pragma unroll
+                for (int r = 0; r < R; ++r) rho[r] = 1.f;
+            }
+            if constexpr (L > 1) {
+                float* bcr = lds + kBcastOff<M> + blk * kPadRow<M>;
+                __syncthreads();
+                if (f) *reinterpret_cast<float4*>(bcr + 4 * k) = make_float4(1.f, 1.f, 1.f, 1.f);
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- export S = exp(X) = min(P U V, 1) ----
+    const bool fvec = ((reinterpret_cast<uintptr_t>(job.frac) & 15u) == 0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        // U_i = N / R_i of the last C1 = N / (rho_i N); 1 on a one-cycle run
+        const float u = (prm.iters > 1) ? fN * rcpf(rho[r] * fN) : 1.0f;
+        float s[M];
+#pragma unroll
+        for (int j = 0; j < M; ++j) s[j] = fminf((P[r][j] * V[j]) * u, 1.0f);
+        float* srow = slot + blk * M * M + (k * R + r) * M;
+#pragma unroll
+        for (int q = 0; q < M / 4; ++q)
+            *reinterpret_cast<float4*>(srow + 4 * q) =
+                make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+        if (job.frac != nullptr && valid) {
+            float* frow = job.frac + (br * M + k * R + r) * job.cols + bc * M;
+            if (fvec) {
+#pragma unroll
+                for (int q = 0; q < M / 4; ++q)
+                    *reinterpret_cast<float4*>(frow + 4 * q) =
+                        make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < M; ++j) frow[j] = s[j];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- round
+// Total order key of entry idx (= i*M + j) with fractional value s: a positive
+// normal double whose high bits are double(s) with the exponent raised by one
+// (so s = 0 stays normal) and whose free low mantissa bits hold MM-1-idx.
+// Larger key = earlier in (s descending, idx ascending).
+template <int M>
+__device__ __forceinline__ double make_key(float s, int idx) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0u;  // -0 -> +0
+    const double d = (double)__uint_as_float(u);
+    const uint64_t b = ((uint64_t)__double_as_longlong(d) + (1ull << 52)) |
+                       (uint64_t)(M * M - 1 - idx);
+    return __longlong_as_double((long long)b);
+}
+template <int M>
+__device__ __forceinline__ int key_index(double key) {
+    return M * M - 1 - (int)((uint32_t)__double_as_longlong(key) & (uint32_t)(M * M - 1));
+}
+
+// Bitonic network, descending, on registers.
+template <int M>
+__device__ __forceinline__ void sort_desc(double (&a)[M]) {
+#pragma unroll
+    for (int size = 2; size <= M; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+            for (int x = 0; x < M; ++x) {
+                const int y = x ^ stride;
+                if (y > x) {
+                    const double hi = fmax(a[x], a[y]), lo = fmin(a[x], a[y]);
+                    if ((x & size) == 0) {
+                        a[x] = hi; a[y] = lo;
+                    } else {
+                        a[x] = lo; a[y] = hi;
+                    }
+                }
+            }
+}
+
+// Walk a sorted row (or column); pb[k] = bit of the entry at sorted position
+// k.  Returns the bits of the entries at positions up to and including the
+// N-th entry whose bit is set in `allowed` -- i.e. every entry whose key is
+// >= the N-th largest allowed key -- or all entries if fewer than N are
+// allowed (threshold "minus infinity").
+template <int M>
+__device__ __forceinline__ uint32_t walk(const uint32_t (&pb)[M], uint32_t allowed, int N) {
+    int cnt = 0;
+    uint32_t m = 0u;
+#pragma unroll
+    for (int k = 0; k < M; ++k) {
+        m |= (cnt < N) ? pb[k] : 0u;
+        cnt += (allowed & pb[k]) != 0u ? 1 : 0;
+    }
+    return cnt < N ? kFull<M> : m;
+}
+
+__device__ __forceinline__ constexpr uint32_t lowmask(int s) {
+    return s == 16 ? 0x0000FFFFu
+         : s == 8  ? 0x00FF00FFu
+         : s == 4  ? 0x0F0F0F0Fu
+         : s == 2  ? 0x33333333u
+                   : 0x55555555u;
+}
+
+// Transpose of the M x M bit matrix held by each aligned group of M lanes
+// (lane i: row i, bit j = column j) -> lane j gets column j (bit i = row i).
+template <int M>
+__device__ __forceinline__ uint32_t transpose_bits(uint32_t x) {
+    const uint32_t lane = threadIdx.x;
+#pragma unroll
+    for (int s = M / 2; s >= 1; s >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)x, s);
+        const uint32_t lo = lowmask(s) & kFull<M>;
+        const uint32_t up = 0u - ((lane >> __builtin_ctz(s)) & 1u);  // all ones on the upper lane
+        // lower lane: keep own low half, take partner's low half into the high half;
+        // upper lane: keep own high half, take partner's high half into the low half.
+        const uint32_t keep = x & (lo ^ up);
+        const uint32_t take = (y & (lo ^ up));
+        x = keep | (((take << s) & ~up) | ((take >> s) & up));
+    }
+    return x;
+}
+
+__device__ __forceinline__ uint32_t float_to_ord(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord_to_float(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int s) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, s);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), s);
+    return ((uint64_t)hi << 32) | lo;
+}
+template <int M>
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
+#pragma unroll
+    for (int s = 1; s < M; s <<= 1) {
+        const uint64_t o = shfl_xor_u64(v, s);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+template <int M>
+__device__ __forceinline__ int group_sum(int v) {
+#pragma unroll
+    for (int s = 1; s < M; s <<= 1) v += __shfl_xor(v, s);
+    return v;
+}
+
+// Rounding of the 64/M blocks handled by this pass: lane (q, i) = block q,
+// row i (and column i).  Sb points at the lane's block (row stride sld).
+template <int M, bool BF16>
+__device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t sld,
+                                           const MatJob& job, int64_t br, int64_t bc, bool valid,
+                                           int ls_steps, float* __restrict__ lds) {
+    constexpr int G = kWave / M;
+    constexpr uint32_t FULL = kFull<M>;
+    const int lane = threadIdx.x;
+    const int q = lane / M, i = lane % M;
+    const int N = job.N;
+
+    // Stage the pass's blocks in LDS (row stride M+1: column reads are
+    // conflict-free), then sort row i and column i by key and keep only the
+    // bit of each sorted entry.
+    float* Ss = lds;  // [G][M][M+1]
+    {
+        float v[M];
+        load_row_f32<M>(Sb + i * sld, (reinterpret_cast<uintptr_t>(Sb) & 15u) == 0 && (sld & 3) == 0, v);
+        float* dst = Ss + (q * M + i) * (M + 1);
+#pragma unroll
+        for (int j = 0; j < M; ++j) dst[j] = valid ? v[j] : 0.f;
+    }
+    __syncthreads();
+    uint32_t rpb[M], cpb[M];
+    {
+        double key[M];
+        const float* src = Ss + (q * M + i) * (M + 1);
+#pragma unroll
+        for (int j = 0; j < M; ++j) key[j] = make_key<M>(src[j], i * M + j);
+        sort_desc<M>(key);
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            rpb[k] = 1u << (key_index<M>(key[k]) % M);
+            asm volatile("" : "+v"(rpb[k]));  // keep only the bit, not the index
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        double key[M];
+        const float* src = Ss + q * M * (M + 1) + i;
+#pragma unroll
+        for (int r = 0; r < M; ++r) key[r] = make_key<M>(src[r * (M + 1)], r * M + i);
+        sort_desc<M>(key);
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            cpb[k] = 1u << (key_index<M>(key[k]) / M);
+            asm volatile("" : "+v"(cpb[k]));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // Ss is reused below
+
+    // ---- greedy as the fixed point of the row / column thresholds ----
+    // Row step: Rmask_i = {j : key_ij >= phi_i}, phi_i = N-th largest key of
+    // row i among j in Amask_i.  Column step: Cmask_j = {i : key_ij >= theta_j},
+    // theta_j = N-th largest key of column j among i with key_ij >= phi_i.
+    // Amask_i = {j : key_ij >= theta_j}.  The theta sequence rises
+    // monotonically from "minus infinity" and can change at most M*M + M
+    // times, so the loop bound is never the exit in exact terms.
+    uint32_t Amask = FULL, Rmask = FULL, Cmask = 0u;
+    for (int round = 0; round <= M * M + M + 2; ++round) {
+        Rmask = walk<M>(rpb, Amask, N);
+        const uint32_t Cnew = walk<M>(cpb, transpose_bits<M>(Rmask), N);
+        const bool changed = Cnew != Cmask;
+        Cmask = Cnew;
+        Amask = transpose_bits<M>(Cmask);
+        if (__ballot(changed) == 0ull) break;
+    }
+    uint32_t Z = Rmask & Amask;  // row i of the greedy mask
+    int r = __popc(Z);
+    int c = __popc(transpose_bits<M>(Z));  // column i count
+    const int shift = q * M;
+    uint32_t DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
+    uint32_t DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
+    int D = group_sum<M>(N - r);
+
+    // ---- local search (R2) and fill (R3) ----
+    const bool need = valid && D > 0;
+    if (__ballot(need) != 0ull) {
+        float* As = lds;                                                   // [G][M][M+1]
+        uint32_t* Zs = reinterpret_cast<uint32_t*>(lds + G * M * (M + 1));  // [G][M]
+        float arow[M];
+        if (valid) {
+            load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, arow);
+        } else {
+#pragma unroll
+            for (int j = 0; j < M; ++j) arow[j] = 0.f;
+        }
+        float* Ai = As + (q * M + i) * (M + 1);
+#pragma unroll
+        for (int j = 0; j < M; ++j) Ai[j] = arow[j];
+        Zs[q * M + i] = Z;
+        __syncthreads();
+
+        int moves = 0;
+        bool active = need && ls_steps > 0;
+        while (__ballot(active) != 0ull) {  // R2
+            uint64_t best = 0;
+            if (active) {
+                for (uint32_t dr = DR; dr; dr &= dr - 1u) {
+                    const int ii = __ffs(dr) - 1;
+                    const uint32_t cand0 = Z & ~Zs[q * M + ii];
+                    if (!cand0) continue;
+                    const float* Aii = As + (q * M + ii) * (M + 1);
+                    for (uint32_t dc = DC; dc; dc &= dc - 1u) {
+                        const int jj = __ffs(dc) - 1;
+                        if ((Z >> jj) & 1u) continue;
+                        const float a2 = Ai[jj];
+                        for (uint32_t cs = cand0; cs; cs &= cs - 1u) {
+                            const int jp = __ffs(cs) - 1;
+                            const float sc = __fsub_rn(__fadd_rn(Aii[jp], a2), Ai[jp]);
+                            const uint32_t lex = (uint32_t)(((ii * M + jj) * M + i) * M + jp);
+                            const uint64_t key =
+                                ((uint64_t)float_to_ord(sc) << 32) | (uint64_t)(0xFFFFFFFFu - lex);
+                            best = key > best ? key : best;
+                        }
+                    }
+                }
+            }
+            best = group_max_u64<M>(best);
+            __syncthreads();
+            if (active) {
+                const float sc = ord_to_float((uint32_t)(best >> 32));
+                if (best == 0ull || !(sc > 0.f)) {
+                    active = false;
+                } else {
+                    const uint32_t lex = 0xFFFFFFFFu - (uint32_t)best;
+                    const int jp = (int)(lex % M), ip = (int)((lex / M) % M);
+                    const int jj = (int)((lex / (M * M)) % M), ii = (int)(lex / (M * M * M));
+                    if (i == ii) { Z |= 1u << jp; r += 1; }
+                    if (i == ip) Z = (Z | (1u << jj)) & ~(1u << jp);
+                    if (i == jj) c += 1;
+                    Zs[q * M + i] = Z;
+                    ++moves;
+                    --D;
+                    if (D == 0 || moves >= ls_steps) active = false;
+                }
+            }
+            __syncthreads();
+            DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
+            DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
+        }
+        active = valid && D > 0;
+        while (__ballot(active) != 0ull) {  // R3
+            uint64_t best = 0;
+            if (active) {
+                const int ii = __ffs(DR) - 1, jj = __ffs(DC) - 1;
+                if (!((Z >> jj) & 1u)) {
+                    const float* Aii = As + (q * M + ii) * (M + 1);
+                    const float a2 = Ai[jj];
+                    for (uint32_t cs = Z & ~Zs[q * M + ii]; cs; cs &= cs - 1u) {
+                        const int jp = __ffs(cs) - 1;
+                        const float sc = __fsub_rn(__fadd_rn(Aii[jp], a2), Ai[jp]);
+                        const uint32_t lex = (uint32_t)(i * M + jp);
+                        const uint64_t key =
+                            ((uint64_t)float_to_ord(sc) << 32) | (uint64_t)(0xFFFFFFFFu - lex);
+                        best = key > best ? key : best;
+                    }
+                }
+            }
+            best = group_max_u64<M>(best);
+            __syncthreads();
+            if (active) {
+                if (best == 0ull) {
+                    active = false;  // unreachable while the invariant holds
+                } else {
+                    const int ii = __ffs(DR) - 1, jj = __ffs(DC) - 1;
+                    const uint32_t lex = 0xFFFFFFFFu - (uint32_t)best;
+                    const int jp = (int)(lex % M), ip = (int)(lex / M);
+                    if (i == ii) { Z |= 1u << jp; r += 1; }
+                    if (i == ip) Z = (Z | (1u << jj)) & ~(1u << jp);
+                    if (i == jj) c += 1;
+                    Zs[q * M + i] = Z;
+                    --D;
+                    if (D == 0) active = false;
+                }
+            }
+            __syncthreads();
+            DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
+            DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
+        }
+    }
+
+    // ---- pack: OR the blocks of one 32-column word together, one store ----
+    const int bit0 = (int)((bc * M) & 31);
+    uint32_t w = valid ? (Z << bit0) : 0u;
+#pragma unroll
+    for (int s = M; s < 32; s <<= 1) w |= (uint32_t)__shfl_xor((int)w, s);
+    if (valid && bit0 == 0) job.mask[(br * M + i) * job.wpr + ((bc * M) >> 5)] = w;
+}
+
+// Whole path for group gl (block-row br, first block column bc0) of one matrix.
+template <int M, bool BF16>
+__device__ __forceinline__ void process_group(const MatJob& job, const Params& prm, int64_t gl,
+                                              float* slot, float* lds) {
+    constexpr int BPG = Geo<M>::BPG, G = kWave / M;
+    const int64_t nbc = job.cols / M;
+    const int64_t gpr = (nbc + BPG - 1) / BPG;
+    const int64_t br = gl / gpr, bc0 = (gl % gpr) * BPG;
+    dykstra_group<M, BF16>(job, prm, br, bc0, slot, lds);
+    __syncthreads();  // slot stores visible to every lane; LDS free for rounding
+#pragma unroll 1
+    for (int p = 0; p < BPG / G; ++p) {
+        const int lb = p * G + (int)threadIdx.x / M;
+        const int64_t bc = bc0 + lb;
+        round_pass<M, BF16>(slot + lb * M * M, M, job, br, bc, bc < nbc, prm.ls_steps, lds);
+        __syncthreads();
+    }
+}
+
+template <int M, bool BF16>
+__global__ __launch_bounds__(kWave) void mask_kernel(MatJob job, Params prm) {
+    __shared__ __attribute__((aligned(16))) float lds[lds_floats<M>()];
+    constexpr int BPG = Geo<M>::BPG;
+    const int64_t nbc = job.cols / M;
+    const int64_t ngroups = (job.rows / M) * ((nbc + BPG - 1) / BPG);
+    float* slot = prm.scratch + (int64_t)blockIdx.x * kSlotFloats;
+    for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x)
+        process_group<M, BF16>(job, prm, g, slot, lds);
+}
+
+template <int M, bool BF16>
+__global__ __launch_bounds__(kWave) void round_kernel(MatJob job, const float* __restrict__ S,
+                                                      int64_t sld, int ls_steps) {
+    __shared__ __attribute__((aligned(16))) float lds[rnd_lds_floats<M>()];
+    constexpr int G = kWave / M;
+    const int64_t nbc = job.cols / M;
+    const int64_t gpr = (nbc + G - 1) / G;
+    const int64_t ngroups = (job.rows / M) * gpr;
+    for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+        const int64_t br = g / gpr;
+        const int64_t bc = (g % gpr) * G + threadIdx.x / M;
+        const bool valid = bc < nbc;
+        const float* Sb = S + br * M * sld + (valid ? bc : 0) * M;
+        round_pass<M, BF16>(Sb, sld, job, br, bc, valid, ls_steps, lds);
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kWave) void batched_kernel(const MatJob* __restrict__ jobs, int count,
+                                                        int64_t total_groups, Params prm) {
+    __shared__ __attribute__((aligned(16))) float lds[kMaxLdsFloats];
+    float* slot = prm.scratch + (int64_t)blockIdx.x * kSlotFloats;
+    for (int64_t g = blockIdx.x; g < total_groups; g += gridDim.x) {
+        int lo = 0, hi = count - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (jobs[mid].group_begin <= g) lo = mid; else hi = mid - 1;
+        }
+        const MatJob job = jobs[lo];
+        const int64_t gl = g - job.group_begin;
+        switch (job.M * 2 + job.bf16) {
+            case 8: process_group<4, false>(job, prm, gl, slot, lds); break;
+            case 9: process_group<4, true>(job, prm, gl, slot, lds); break;
+            case 16: process_group<8, false>(job, prm, gl, slot, lds); break;
+            case 17: process_group<8, true>(job, prm, gl, slot, lds); break;
+            case 32: process_group<16, false>(job, prm, gl, slot, lds); break;
+            case 33: process_group<16, true>(job, prm, gl, slot, lds); break;
+            case 64: process_group<32, false>(job, prm, gl, slot, lds); break;
+            case 65: process_group<32, true>(job, prm, gl, slot, lds); break;
+            default: break;
+        }
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- host side
+#define TSENOR_DISPATCH(M_, BF, CALL)                                   \
+    do {                                                                \
+        switch ((M_) * 2 + ((BF) ? 1 : 0)) {                            \
+            case 8: { constexpr int MM = 4; constexpr bool B = false; CALL; } break;  \
+            case 9: { constexpr int MM = 4; constexpr bool B = true; CALL; } break;   \
+            case 16: { constexpr int MM = 8; constexpr bool B = false; CALL; } break; \
+            case 17: { constexpr int MM = 8; constexpr bool B = true; CALL; } break;  \
+            case 32: { constexpr int MM = 16; constexpr bool B = false; CALL; } break; \
+            case 33: { constexpr int MM = 16; constexpr bool B = true; CALL; } break;  \
+            case 64: { constexpr int MM = 32; constexpr bool B = false; CALL; } break; \
+            case 65: { constexpr int MM = 32; constexpr bool B = true; CALL; } break;  \
+            default: return (int)hipErrorInvalidValue;                  \
+        }                                                               \
+    } while (0)
+
+int launch_mask(const MatJob& job, const Params& prm, int grid, void* stream) {
+    TSENOR_DISPATCH(job.M, job.bf16,
+                    hipLaunchKernelGGL((mask_kernel<MM, B>), dim3(grid), dim3(kWave), 0,
+                                       (hipStream_t)stream, job, prm));
+    return (int)hipGetLastError();
+}
+
+int launch_round(const MatJob& job, const float* S, int64_t lds, int ls_steps, int grid,
+                 void* stream) {
+    TSENOR_DISPATCH(job.M, job.bf16,
+                    hipLaunchKernelGGL((round_kernel<MM, B>), dim3(grid), dim3(kWave), 0,
+                                       (hipStream_t)stream, job, S, lds, ls_steps));
+    return (int)hipGetLastError();
+}
+
+int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int /*max_m*/,
+                   const Params& prm, int grid, void* stream) {
+    hipLaunchKernelGGL(batched_kernel, dim3(grid), dim3(kWave), 0, (hipStream_t)stream, jobs_dev,
+                       count, total_groups, prm);
+    return (int)hipGetLastError();
+}
+
+int occupancy_mask(int M, int bf16) {
+    int n = 0;
+    TSENOR_DISPATCH(M, bf16,
+                    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mask_kernel<MM, B>,
+                                                                       kWave, 0));
+    return n;
+}
+
+int occupancy_round(int M, int bf16) {
+    int n = 0;
+    TSENOR_DISPATCH(M, bf16,
+                    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, round_kernel<MM, B>,
+                                                                       kWave, 0));
+    return n;
+}
+
+int occupancy_batched() {
+    int n = 0;
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, batched_kernel, kWave, 0);
+    return n;
+}
+
+}  // namespace tsenor

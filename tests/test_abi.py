@@ -1,0 +1,93 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/tsenor.h, and rejects every invalid argument with its status
+code before touching the device (no HIP call is made on these paths)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_mask_search_amd as sms
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsenor.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced on the rejected paths
+
+OK, NULL, SHAPE, NM, PARAM, DTYPE, HIP = range(7)
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(tsenor_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared()
+    assert names == ["tsenor_last_error", "tsenor_mask", "tsenor_mask_batched", "tsenor_round",
+                     "tsenor_status_str", "tsenor_version"]
+    out = subprocess.check_output(["nm", "-D", "--defined-only", sms.library_path()], text=True)
+    exported = set(re.findall(r"\bT (tsenor_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(sms.lib(), n)
+
+
+def test_status_strings():
+    l = sms.lib()
+    for s in range(7):
+        assert l.tsenor_status_str(s).decode()
+    assert l.tsenor_status_str(99).decode() == "unknown status"
+    assert sms.version() == 0x000100
+
+
+def _mask(W=FAKE, dtype=1, rows=64, cols=64, ld=64, N=2, M=4, tau=20.0, iters=10, ls=4,
+          mask=FAKE, frac=None):
+    return sms.lib().tsenor_mask(W, dtype, rows, cols, ld, N, M, tau, iters, ls, mask, frac, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), NULL), (dict(mask=None), NULL),
+    (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(M=6, N=3), NM), (dict(M=64, N=8), NM), (dict(N=0), NM), (dict(N=5), NM),
+    (dict(rows=0), SHAPE), (dict(cols=-4), SHAPE), (dict(rows=66), SHAPE), (dict(cols=62), SHAPE),
+    (dict(ld=60), SHAPE),
+    (dict(tau=-1.0), PARAM), (dict(tau=math.inf), PARAM), (dict(tau=math.nan), PARAM),
+    (dict(iters=0), PARAM), (dict(ls=-1), PARAM),
+])
+def test_mask_rejects(kw, code):
+    assert _mask(**kw) == code
+
+
+def test_round_rejects():
+    l = sms.lib()
+    r = lambda S=FAKE, lds=64, W=FAKE, dt=0, rows=64, cols=64, ld=64, N=2, M=4, ls=2, mask=FAKE: \
+        l.tsenor_round(S, lds, W, dt, rows, cols, ld, N, M, ls, mask, None)
+    assert r(S=None) == NULL
+    assert r(W=None) == NULL
+    assert r(mask=None) == NULL
+    assert r(lds=32) == SHAPE
+    assert r(ls=-3) == PARAM
+    assert r(M=12) == NM
+    assert r(dt=7) == DTYPE
+
+
+def test_batched_rejects():
+    l = sms.lib()
+    M = sms._lib._Matrix
+    good = M(0x1000, 1, 64, 64, 64, 8, 16, 0x1000, 0)
+    bad = M(0x1000, 1, 64, 60, 64, 8, 16, 0x1000, 0)
+    arr = (M * 2)(good, bad)
+    assert l.tsenor_mask_batched(arr, 2, 20.0, 5, 2, None) == SHAPE
+    assert l.tsenor_mask_batched(arr, -1, 20.0, 5, 2, None) == PARAM
+    assert l.tsenor_mask_batched(None, 3, 20.0, 5, 2, None) == NULL
+    assert l.tsenor_mask_batched(arr, 1, -2.0, 5, 2, None) == PARAM
+    assert l.tsenor_mask_batched(arr, 1, 20.0, 0, 2, None) == PARAM
+    assert l.tsenor_mask_batched(None, 0, 20.0, 5, 2, None) == OK  # empty batch: no-op
+
+
+def test_binding_requires_device_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(TypeError):
+        sms.mask(torch.zeros(8, 8), 2, 4, 20.0, 5, 2)

@@ -1,0 +1,222 @@
+"""GPU parity: the HIP path against the oracle on the same seeded inputs.
+
+Bars (the method as in the pith.science review of TSENOR, "What carries the
+argument"; tolerances from the design): fractional S within 1e-4 max-abs of the
+fp64 oracle; masks bit-exact with the oracle's rounding applied to the GPU's S,
+and with the GPU's own rounding-only entry point on that S; every block
+feasible (N ones per row and column).  Small cases span several groups, a
+ragged last group and a partial last mask word; the workload-sized cases check
+sampled blocks (S) and whole block-rows (masks) at full size, in the launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import sparse_mask_search_amd as sms
+from sparse_mask_search_amd import workloads as wl
+from gpu_util import (as_f32, assert_feasible, gather_blocks, sample_block_ids, to_device,
+                      words)
+
+pytestmark = pytest.mark.gpu
+S_TOL = 1e-4
+
+
+def _note(*a):
+    print("[case]", *a, flush=True)
+
+
+def _run(W_np, N, M, tau, iters, ls):
+    import torch
+    W = to_device(W_np)
+    mask, S = sms.mask(W, N, M, tau, iters, ls, return_frac=True)
+    mask2 = sms.round_mask(S, W, N, M, ls)
+    torch.cuda.synchronize()
+    return W, words(mask), S.cpu().numpy(), words(mask2)
+
+
+def _small(seed, M, nbc, nbr, kind, bf16):
+    rng = np.random.default_rng(seed)
+    W = wl.random_blocks(seed, nbc, M, kind)
+    W = np.concatenate([W] + [wl.random_blocks(seed * 7 + r, nbc, M, kind) for r in range(1, nbr)])
+    if kind != "zero":
+        W[:M, :M] = 0.0  # one all-zero block
+    W = W.astype(np.float32)
+    return wl.f32_to_bf16_bits(W) if bf16 else W
+
+
+SMALL = [  # M, blocks per row (ragged vs the group width), block rows
+    (4, 70, 3), (8, 67, 2), (16, 37, 3), (32, 19, 2),
+]
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("kind", ["student_t", "outlier", "ties"])
+@pytest.mark.parametrize("M,nbc,nbr", SMALL)
+def test_small_parity(M, nbc, nbr, kind, bf16):
+    N = M // 2
+    tau, iters, ls = (20.0, 60, M)
+    W_np = _small(100 + M, M, nbc, nbr, kind, bf16)
+    rows, cols = W_np.shape
+    _note(f"small M={M} {rows}x{cols} {kind} bf16={bf16}")
+    _, mask, S, mask2 = _run(W_np, N, M, tau, iters, ls)
+    Wf = as_f32(W_np)
+    S64, _ = oracle.dykstra(Wf, N, M, tau, iters)
+    assert np.abs(S - S64).max() < S_TOL
+    ref, _ = oracle.round_matrix(S, Wf, N, M, ls)
+    assert np.array_equal(mask, ref)
+    assert np.array_equal(mask2, ref)
+    assert_feasible(mask, rows, cols, N, M)
+
+
+@pytest.mark.parametrize("M,N", [(4, 1), (8, 3), (16, 5), (32, 7), (32, 31), (16, 16)])
+def test_other_n(M, N):
+    W_np = _small(7 + N, M, 11, 2, "student_t", True)
+    rows, cols = W_np.shape
+    _note(f"N={N} M={M} {rows}x{cols}")
+    _, mask, S, mask2 = _run(W_np, N, M, 15.0, 40, 5)
+    Wf = as_f32(W_np)
+    S64, _ = oracle.dykstra(Wf, N, M, 15.0, 40)
+    assert np.abs(S - S64).max() < S_TOL
+    ref, _ = oracle.round_matrix(S, Wf, N, M, 5)
+    assert np.array_equal(mask, ref) and np.array_equal(mask2, ref)
+    assert_feasible(mask, rows, cols, N, M)
+
+
+@pytest.mark.parametrize("M", [4, 8, 16, 32])
+def test_closed_forms(M):
+    """tau = 0: S = N/M everywhere and the mask is the block diagonal of N x N
+    tiles; one iteration and no local search also match the oracle."""
+    N = M // 2
+    W_np = _small(3, M, 9, 2, "normal", False)
+    rows, cols = W_np.shape
+    _note(f"tau=0 M={M}")
+    _, mask, S, _ = _run(W_np, N, M, 0.0, 7, 3)
+    assert np.allclose(S, N / M, rtol=2e-6, atol=0)
+    diag = np.zeros((M, M), bool)
+    for k in range(M // N):
+        diag[k * N:(k + 1) * N, k * N:(k + 1) * N] = True
+    Z = oracle.unpack_mask(mask, cols)
+    for bi in range(rows // M):
+        for bj in range(cols // M):
+            assert np.array_equal(Z[bi * M:(bi + 1) * M, bj * M:(bj + 1) * M], diag)
+    _note(f"iters=1 ls=0 M={M}")
+    _, mask, S, mask2 = _run(W_np, N, M, 25.0, 1, 0)
+    S64, _ = oracle.dykstra(W_np, N, M, 25.0, 1)
+    assert np.abs(S - S64).max() < S_TOL
+    ref, _ = oracle.round_matrix(S, W_np, N, M, 0)
+    assert np.array_equal(mask, ref) and np.array_equal(mask2, ref)
+
+
+def test_strided_and_unaligned_rows():
+    """ld > cols and an odd ld (scalar-load path) give the same result as the
+    packed matrix."""
+    import torch
+    M, N = 16, 8
+    W_np = _small(5, M, 9, 2, "student_t", True)
+    rows, cols = W_np.shape
+    for extra in (16, 3):
+        _note(f"ld=cols+{extra}")
+        big = np.zeros((rows, cols + extra), np.uint16)
+        big[:, :cols] = W_np
+        Wb = to_device(big)[:, :cols]
+        m1, s1 = sms.mask(Wb, N, M, 20.0, 30, 8, return_frac=True)
+        m0, s0 = sms.mask(to_device(W_np), N, M, 20.0, 30, 8, return_frac=True)
+        torch.cuda.synchronize()
+        assert torch.equal(m1, m0) and torch.equal(s1, s0)
+
+
+def test_deterministic_and_frac_independent():
+    import torch
+    M, N = 32, 16
+    W = to_device(_small(9, M, 19, 2, "outlier", True))
+    _note("determinism")
+    a, sa = sms.mask(W, N, M, 40.0, 50, 32, return_frac=True)
+    b, _ = sms.mask(W, N, M, 40.0, 50, 32)
+    c, sc = sms.mask(W, N, M, 40.0, 50, 32, return_frac=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c) and torch.equal(sa, sc)
+
+
+# ---------------------------------------------------------------- workloads
+
+def _workload(name):
+    w = wl.WORKLOADS[name]
+    W_np = wl.generate(name)
+    return w, W_np, as_f32(W_np)
+
+
+def test_workload_2_4_full():
+    """2:4 on 1024x1024 fp32: every block against the oracle, plus each
+    block's brute-force optimum over the 90 feasible masks (gap reported)."""
+    w, W_np, Wf = _workload("2:4-1024x1024-f32")
+    _note(w.name)
+    _, mask, S, mask2 = _run(W_np, w.N, w.M, w.tau, w.iters, w.ls_steps)
+    S64, _ = oracle.dykstra(Wf, w.N, w.M, w.tau, w.iters)
+    assert np.abs(S - S64).max() < S_TOL
+    ref, _ = oracle.round_matrix(S, Wf, w.N, w.M, w.ls_steps)
+    assert np.array_equal(mask, ref) and np.array_equal(mask2, ref)
+    assert_feasible(mask, w.rows, w.cols, w.N, w.M)
+    masks = oracle.feasible_masks(4, 2).astype(np.float64)
+    A = oracle.block_view(np.abs(Wf.astype(np.float64)), 4).reshape(-1, 4, 4)
+    Z = oracle.block_view(oracle.unpack_mask(mask, w.cols).astype(np.float64), 4).reshape(-1, 4, 4)
+    opt = np.einsum("kij,bij->bk", masks, A).max(1)
+    got = (Z * A).sum((1, 2))
+    assert (got <= opt + 1e-9).all()
+    gap = (opt - got) / np.where(opt > 0, opt, 1)
+    print(f"2:4 gap vs brute force: mean {gap.mean():.4%} max {gap.max():.4%} "
+          f"optimal {np.mean(gap < 1e-12):.2%}", flush=True)
+
+
+@pytest.mark.parametrize("name,nsample,slab_rows", [
+    ("4:8-4096x4096-f32", 3000, 512),
+    ("8:16-4096x11008-bf16", 1500, 256),
+    ("16:32-8192x28672-bf16", 400, 128),
+])
+def test_workload_sampled(name, nsample, slab_rows):
+    w, W_np, Wf = _workload(name)
+    _note(w.name)
+    import torch
+    W = to_device(W_np)
+    mask_t, S_t = sms.mask(W, w.N, w.M, w.tau, w.iters, w.ls_steps, return_frac=True)
+    mask2_t = sms.round_mask(S_t, W, w.N, w.M, w.ls_steps)
+    torch.cuda.synchronize()
+    mask = words(mask_t)
+    assert np.array_equal(mask, words(mask2_t))
+    assert_feasible(mask, w.rows, w.cols, w.N, w.M)
+    ids = sample_block_ids(w.blocks, nsample, 11)
+    S64, _ = oracle.dykstra_blocks(Wf, w.N, w.M, w.tau, w.iters, ids)
+    rows_needed = sorted({int(b) // (w.cols // w.M) for b in ids})
+    S = S_t.cpu().numpy()
+    Sg = gather_blocks(S, w.M, ids, w.cols)
+    err = np.abs(Sg - S64).max()
+    print(f"{w.name}: max|S-S64| over {len(ids)} blocks = {err:.3e}", flush=True)
+    assert err < S_TOL
+    for r0 in (0, w.rows - slab_rows):  # whole block-rows at both edges
+        ref, _ = oracle.round_matrix(S[r0:r0 + slab_rows], Wf[r0:r0 + slab_rows], w.N, w.M,
+                                     w.ls_steps)
+        assert np.array_equal(mask[r0:r0 + slab_rows], ref)
+    del rows_needed
+
+
+def test_model7b_layer_batched():
+    """One batched launch over a 7B-shaped layer (8:16 attention, 16:32 MLP)
+    equals per-matrix calls bit for bit, and sampled blocks match the oracle."""
+    import torch
+    mats = list(wl.model7b_layer(0))
+    _note("7B layer 0 batched")
+    Ws = [to_device(b) for (_, _, _, b) in mats]
+    outs = sms.mask_batched([(W, N, M) for W, (_, N, M, _) in zip(Ws, mats)], wl.MODEL7B_TAU,
+                            wl.MODEL7B_ITERS, wl.MODEL7B_LS, return_frac=True)
+    torch.cuda.synchronize()
+    for W, (nm, N, M, bits), (m, f) in zip(Ws, mats, outs):
+        m1, f1 = sms.mask(W, N, M, wl.MODEL7B_TAU, wl.MODEL7B_ITERS, wl.MODEL7B_LS,
+                          return_frac=True)
+        torch.cuda.synchronize()
+        assert torch.equal(m, m1) and torch.equal(f, f1), nm
+        rows, cols = W.shape
+        assert_feasible(words(m), rows, cols, N, M)
+        Wf = as_f32(bits)
+        ids = sample_block_ids((rows // M) * (cols // M), 60, 3)
+        S64, _ = oracle.dykstra_blocks(Wf, N, M, wl.MODEL7B_TAU, wl.MODEL7B_ITERS, ids)
+        assert np.abs(gather_blocks(f.cpu().numpy(), M, ids, cols) - S64).max() < S_TOL, nm
