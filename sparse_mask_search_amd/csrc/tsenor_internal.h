@@ -30,9 +30,9 @@ struct Params {
 constexpr int kWave = 64;
 constexpr int64_t kSlotFloats = 8192;  // 32 KiB: max over M of blocks_per_group * M * M
 
-// Blocks per group: M=32 -> 8 (8 lanes per block), M=16 -> 16 (4 lanes per
-// block), M=8 and M=4 -> 64 (one lane per block).
-inline int blocks_per_group(int M) { return M == 32 ? 8 : (M == 16 ? 16 : 64); }
+// Blocks per group of the fused kernel for pattern size M (the solve layout
+// is fixed per M in tsenor_kernels.hip).
+int blocks_per_group(int M);
 
 // Host-side launchers (tsenor_kernels.hip).  They return a hipError_t value.
 int launch_mask(const MatJob& job, const Params& prm, int grid, void* stream);

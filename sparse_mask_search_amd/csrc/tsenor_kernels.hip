@@ -48,20 +48,37 @@
 namespace tsenor {
 namespace {
 
-// Rows per lane (R), lanes per block (L) and blocks per group (BPG) for the solve.
+// Solve layout: each lane holds an R x CW tile (R rows, CW = M/H columns) of
+// one block, a block spans L = (M/R)*H lanes and a group is BPG = 64/L
+// blocks.  Row sums are completed across the H lanes of a row group by DPP,
+// column sums across the G = M/R row groups through LDS.
 template <int M> struct Geo;
-template <> struct Geo<4> { static constexpr int R = 4, L = 1, BPG = 64; };
-template <> struct Geo<8> { static constexpr int R = 8, L = 1, BPG = 64; };
-template <> struct Geo<16> { static constexpr int R = 4, L = 4, BPG = 16; };
-template <> struct Geo<32> { static constexpr int R = 4, L = 8, BPG = 8; };
+template <> struct Geo<4> { static constexpr int R = 4, H = 1; };
+template <> struct Geo<8> { static constexpr int R = 8, H = 1; };
+template <> struct Geo<16> { static constexpr int R = 4, H = 1; };
+template <> struct Geo<32> { static constexpr int R = 8, H = 2; };
+template <int M> constexpr int kR = Geo<M>::R;
+template <int M> constexpr int kH = Geo<M>::H;
+template <int M> constexpr int kCW = M / kH<M>;         // columns per lane
+template <int M> constexpr int kG = M / kR<M>;           // row groups per block
+template <int M> constexpr int kL = kG<M> * kH<M>;       // lanes per block
+template <int M> constexpr int kBPG = kWave / kL<M>;     // blocks per group
+template <int M> constexpr int kCPL = M / kL<M>;         // columns finalised per lane
+template <int M> constexpr int kRowsPerSched = 1;        // rows scheduled together in the loop
+static_assert(kBPG<32> * 32 % 32 == 0 && kBPG<16> * 16 % 32 == 0, "groups cover whole words");
 
-template <int M> constexpr int kPadRow = M + 4;                          // floats per lane row
-template <int M> constexpr int kBlkStride = Geo<M>::L * kPadRow<M>;     // floats per block
-template <int M> constexpr int kBcastOff = Geo<M>::BPG * kBlkStride<M>;  // start of V broadcast
+template <int M> constexpr int kRowStride = M + 4;                      // floats per partial row
+template <int M> constexpr int kBlkStride = kG<M> * kRowStride<M>;      // floats per block
+template <int M> constexpr int kBcastOff = kBPG<M> * kBlkStride<M>;     // start of V rows
 template <int M> constexpr int dyk_lds_floats() {
-    return Geo<M>::L == 1 ? 0 : kBcastOff<M> + Geo<M>::BPG * kPadRow<M>;
+    return kL<M> == 1 ? 0 : kBcastOff<M> + kBPG<M> * kRowStride<M>;
 }
-template <int M> constexpr int rnd_lds_floats() { return (kWave / M) * M * (M + 1) + kWave; }
+// Rounding staging: block q of a pass at q*kStageBlk, row i at i*(M+4); the
+// block stride is M (mod 32) apart so that column reads of the blocks that
+// share a 32-lane half hit distinct banks.
+template <int M> constexpr int kStageRow = M + 4;
+template <int M> constexpr int kStageBlk = M * (M + 4) + (M < 32 ? M : 0);
+template <int M> constexpr int rnd_lds_floats() { return (kWave / M) * kStageBlk<M> + kWave; }
 template <int M> constexpr int lds_floats() {
     return dyk_lds_floats<M>() > rnd_lds_floats<M>() ? dyk_lds_floats<M>() : rnd_lds_floats<M>();
 }
@@ -148,57 +165,83 @@ __device__ __forceinline__ float tree_sum(const float (&v)[M]) {
     return s[0];
 }
 
-// Column totals of a block whose rows are spread over L lanes: every lane
-// writes its M partials, lane k of the block adds up columns [4k, 4k+4) and
-// stores them to the block's broadcast row, which every lane then reads.
-// With kind == 0 the totals are broadcast as they are (combine = max or sum);
-// kind == 1 turns each total C_j into V_j * N / C_j, V_j being the value
-// currently in the broadcast row (so V never needs dynamic register indexing).
-// Returns, for kind == 1, whether any of this lane's four new V_j left
+// Sum / max of x over the H lanes of a row group (adjacent lanes), by DPP.
+template <int H, bool MAXOP>
+__device__ __forceinline__ float row_allreduce(float x) {
+    if constexpr (H >= 2) {
+        const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+        x = MAXOP ? fmaxf(x, y) : x + y;  // quad_perm [1,0,3,2]: lane ^ 1
+    }
+    if constexpr (H >= 4) {
+        const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+        x = MAXOP ? fmaxf(x, y) : x + y;  // quad_perm [2,3,0,1]: lane ^ 2
+    }
+    static_assert(H == 1 || H == 2 || H == 4, "H");
+    return x;
+}
+
+// Column totals of a block whose rows are spread over G row groups: lane
+// (g, h) writes its CW partials to row g, columns [h*CW, h*CW + CW); lane lb
+// of the block combines columns [lb*CPL, lb*CPL + CPL) over the G rows and
+// stores them to the block's broadcast row, from which every lane reads its
+// own CW columns.  KIND 0 broadcasts the totals (combine = max or sum);
+// KIND 1 turns each total C_j into V_j * N / C_j with V_j the value currently
+// in the broadcast row, and returns whether any new V_j of this lane left
 // [2^-40, 2^40].
 template <int M, int KIND, bool MAXOP>
-__device__ __forceinline__ bool col_exchange(const float (&part)[M], float (&out)[M], float* lds,
-                                             int blk, int k, float fN) {
-    constexpr int L = Geo<M>::L;
-    static_assert(M / L == 4, "one float4 of columns per lane");
-    float* mine = lds + blk * kBlkStride<M> + k * kPadRow<M>;
+__device__ __forceinline__ bool col_exchange(const float (&part)[kCW<M>], float (&out)[kCW<M>],
+                                             float* lds, int blk, int lb, float fN) {
+    constexpr int CW = kCW<M>, G = kG<M>, H = kH<M>, CPL = kCPL<M>;
+    const int g = lb / H, h = lb % H;
+    float* mine = lds + blk * kBlkStride<M> + g * kRowStride<M> + h * CW;
 #pragma unroll
-    for (int q = 0; q < M / 4; ++q)
+    for (int q = 0; q < CW / 4; ++q)
         *reinterpret_cast<float4*>(mine + 4 * q) =
             make_float4(part[4 * q], part[4 * q + 1], part[4 * q + 2], part[4 * q + 3]);
     __syncthreads();
-    const float* base = lds + blk * kBlkStride<M> + 4 * k;
-    float4 acc = *reinterpret_cast<const float4*>(base);
+    const float* base = lds + blk * kBlkStride<M> + lb * CPL;
+    float acc[CPL];
 #pragma unroll
-    for (int kk = 1; kk < L; ++kk) {
-        const float4 v = *reinterpret_cast<const float4*>(base + kk * kPadRow<M>);
-        if constexpr (MAXOP) {
-            acc.x = fmaxf(acc.x, v.x); acc.y = fmaxf(acc.y, v.y);
-            acc.z = fmaxf(acc.z, v.z); acc.w = fmaxf(acc.w, v.w);
-        } else {
-            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    for (int c = 0; c < CPL; ++c) acc[c] = base[c];
+#pragma unroll
+    for (int gg = 1; gg < G; ++gg)
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const float v = base[gg * kRowStride<M> + c];
+            acc[c] = MAXOP ? fmaxf(acc[c], v) : acc[c] + v;
         }
-    }
-    float* bc = lds + kBcastOff<M> + blk * kPadRow<M>;
+    float* bc = lds + kBcastOff<M> + blk * kRowStride<M>;
     bool bad = false;
     if constexpr (KIND == 1) {
-        const float4 vo = *reinterpret_cast<const float4*>(bc + 4 * k);
-        acc.x = vo.x * (fN * rcpf(acc.x));
-        acc.y = vo.y * (fN * rcpf(acc.y));
-        acc.z = vo.z * (fN * rcpf(acc.z));
-        acc.w = vo.w * (fN * rcpf(acc.w));
-        const float lo = fminf(fminf(acc.x, acc.y), fminf(acc.z, acc.w));
-        const float hi = fmaxf(fmaxf(acc.x, acc.y), fmaxf(acc.z, acc.w));
+        float lo = 0x1p40f, hi = 0x1p-40f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            acc[c] = bc[lb * CPL + c] * (fN * rcpf(acc[c]));
+            lo = fminf(lo, acc[c]);
+            hi = fmaxf(hi, acc[c]);
+        }
         bad = !(lo >= 0x1p-40f && hi <= 0x1p40f);
     }
-    *reinterpret_cast<float4*>(bc + 4 * k) = acc;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) bc[lb * CPL + c] = acc[c];
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < M / 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(bc + 4 * q);
+    for (int q = 0; q < CW / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(bc + h * CW + 4 * q);
         out[4 * q] = v.x; out[4 * q + 1] = v.y; out[4 * q + 2] = v.z; out[4 * q + 3] = v.w;
     }
     return bad;
+}
+
+// Register-level ordering point: an empty asm that "reads and writes" a and
+// b.  Every later use of a/b waits for it and every earlier write of a/b
+// precedes it.  Emits no instruction.
+template <int CW>
+__device__ __forceinline__ void order_fence(float (&a)[CW], float (&b)[CW]) {
+#pragma unroll
+    for (int c = 0; c < CW; c += 4)
+        asm volatile("" : "+v"(a[c]), "+v"(a[c + 1]), "+v"(a[c + 2]), "+v"(a[c + 3]),
+                          "+v"(b[c]), "+v"(b[c + 1]), "+v"(b[c + 2]), "+v"(b[c + 3]));
 }
 
 // ---------------------------------------------------------------- solve
@@ -208,9 +251,10 @@ template <int M, bool BF16>
 __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& prm, int64_t br,
                                               int64_t bc0, float* __restrict__ slot,
                                               float* __restrict__ lds) {
-    constexpr int R = Geo<M>::R, L = Geo<M>::L;
+    constexpr int R = kR<M>, H = kH<M>, CW = kCW<M>, L = kL<M>;
     const int lane = threadIdx.x;
-    const int blk = lane / L, k = lane % L;
+    const int blk = lane / L, lb = lane % L;
+    const int g = lb / H, h = lb % H;
     const int64_t nbc = job.cols / M;
     const int64_t bc = bc0 + blk;
     const bool valid = bc < nbc;
@@ -218,15 +262,17 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     const float invN = 1.0f / fN;
     const float log2N = log2f(fN);
     const bool vec = job.aligned != 0;
+    const int64_t row0 = br * M + g * R;      // first matrix row of this lane's tile
+    const int64_t col0 = bc * M + h * CW;     // first matrix column of this lane's tile
 
-    float P[R][M];
+    float P[R][CW];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if (valid) {
-            load_abs_row<M, BF16>(job.W, (br * M + k * R + r) * job.ld + bc * M, vec, P[r]);
+            load_abs_row<CW, BF16>(job.W, (row0 + r) * job.ld + col0, vec, P[r]);
         } else {
 #pragma unroll
-            for (int j = 0; j < M; ++j) P[r][j] = 0.f;
+            for (int c = 0; c < CW; ++c) P[r][c] = 0.f;
         }
     }
     // scores What = A / max(A); X = tau * What in log2 units
@@ -234,91 +280,100 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int j = 0; j < M; ++j) m = fmaxf(m, P[r][j]);
+        for (int c = 0; c < CW; ++c) m = fmaxf(m, P[r][c]);
 #pragma unroll
     for (int s = 1; s < L; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
     const float scale = (m > 0.f) ? prm.tau_log2e / m : 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int j = 0; j < M; ++j) P[r][j] *= scale;
+        for (int c = 0; c < CW; ++c) P[r][c] *= scale;
 
     // ---- cycle 1 in log2 space (Q = 0, so no clip enters C1/C2) ----
 #pragma unroll
     for (int r = 0; r < R; ++r) {  // C1
         float mx = P[r][0];
 #pragma unroll
-        for (int j = 1; j < M; ++j) mx = fmaxf(mx, P[r][j]);
-        float e[M];
+        for (int c = 1; c < CW; ++c) mx = fmaxf(mx, P[r][c]);
+        mx = row_allreduce<H, true>(mx);
+        float e[CW];
 #pragma unroll
-        for (int j = 0; j < M; ++j) e[j] = ex2(P[r][j] - mx);
-        const float a = log2N - mx - lg2(tree_sum<M>(e));
+        for (int c = 0; c < CW; ++c) e[c] = ex2(P[r][c] - mx);
+        const float a = log2N - mx - lg2(row_allreduce<H, false>(tree_sum<CW>(e)));
 #pragma unroll
-        for (int j = 0; j < M; ++j) P[r][j] += a;
+        for (int c = 0; c < CW; ++c) P[r][c] += a;
     }
     {  // C2: column max, then column sum of 2^(x - max)
-        float part[M], cmax[M], csum[M];
+        float part[CW], cmax[CW], csum[CW];
 #pragma unroll
-        for (int j = 0; j < M; ++j) {
-            float v = P[0][j];
+        for (int c = 0; c < CW; ++c) {
+            float v = P[0][c];
 #pragma unroll
-            for (int r = 1; r < R; ++r) v = fmaxf(v, P[r][j]);
-            part[j] = v;
+            for (int r = 1; r < R; ++r) v = fmaxf(v, P[r][c]);
+            part[c] = v;
         }
         if constexpr (L == 1) {
 #pragma unroll
-            for (int j = 0; j < M; ++j) cmax[j] = part[j];
+            for (int c = 0; c < CW; ++c) cmax[c] = part[c];
         } else {
-            col_exchange<M, 0, true>(part, cmax, lds, blk, k, fN);
+            col_exchange<M, 0, true>(part, cmax, lds, blk, lb, fN);
         }
 #pragma unroll
-        for (int j = 0; j < M; ++j) {
+        for (int c = 0; c < CW; ++c) {
             float v = 0.f;
 #pragma unroll
-            for (int r = 0; r < R; ++r) v += ex2(P[r][j] - cmax[j]);
-            part[j] = v;
+            for (int r = 0; r < R; ++r) v += ex2(P[r][c] - cmax[c]);
+            part[c] = v;
         }
         if constexpr (L == 1) {
 #pragma unroll
-            for (int j = 0; j < M; ++j) csum[j] = part[j];
+            for (int c = 0; c < CW; ++c) csum[c] = part[c];
         } else {
-            col_exchange<M, 0, false>(part, csum, lds, blk, k, fN);
+            col_exchange<M, 0, false>(part, csum, lds, blk, lb, fN);
         }
         // C3 of cycle 1 is carried by P = 2^Y: X = min(Y, 0) appears as min(P V U, 1)
 #pragma unroll
-        for (int j = 0; j < M; ++j) {
-            const float b = log2N - cmax[j] - lg2(csum[j]);
+        for (int c = 0; c < CW; ++c) {
+            const float b = log2N - cmax[c] - lg2(csum[c]);
 #pragma unroll
-            for (int r = 0; r < R; ++r) P[r][j] = ex2(P[r][j] + b);
+            for (int r = 0; r < R; ++r) P[r][c] = ex2(P[r][c] + b);
         }
     }
 
     // ---- cycles 2..T in scaling form ----
-    float V[M], rho[R];
+    float V[CW], rho[R];
 #pragma unroll
-    for (int j = 0; j < M; ++j) V[j] = 1.f;
+    for (int c = 0; c < CW; ++c) V[c] = 1.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) rho[r] = 1.f;
     if constexpr (L > 1) {
-        float* bcr = lds + kBcastOff<M> + blk * kPadRow<M>;
-        *reinterpret_cast<float4*>(bcr + 4 * k) = make_float4(1.f, 1.f, 1.f, 1.f);
+        float* bcr = lds + kBcastOff<M> + blk * kRowStride<M>;
+#pragma unroll
+        for (int c = 0; c < kCPL<M>; ++c) bcr[lb * kCPL<M> + c] = 1.f;
         // made visible by the first exchange's barrier
     }
     for (int it = 1; it < prm.iters; ++it) {
-        float cacc[M];
+        float cacc[CW];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float t[M], acc[4] = {0.f, 0.f, 0.f, 0.f};
+            float t[CW];
+            float acc[4];
 #pragma unroll
-            for (int j = 0; j < M; ++j) {
-                t[j] = fminf(P[r][j] * V[j], rho[r]);
-                acc[j & 3] += t[j];
+            for (int c = 0; c < CW; ++c) {
+                t[c] = fminf(P[r][c] * V[c], rho[r]);
+                acc[c & 3] = (c < 4) ? t[c] : acc[c & 3] + t[c];
             }
-            const float rs = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            const float rs = row_allreduce<H, false>((acc[0] + acc[1]) + (acc[2] + acc[3]));
             const float u = fN * rcpf(rs);
             rho[r] = rs * invN;
 #pragma unroll
-            for (int j = 0; j < M; ++j) cacc[j] = (r == 0) ? t[j] * u : fmaf(t[j], u, cacc[j]);
+            for (int c = 0; c < CW; ++c) cacc[c] = (r == 0) ? t[c] * u : fmaf(t[c], u, cacc[c]);
+            // Keep one row's temporaries live at a time: left alone, the
+            // instruction selector hoists every row's products and spills the
+            // tile.  The empty asm claims to update cacc and V, so this row's
+            // column updates complete before, and the next row's products
+            // start after, this point.  No instruction is emitted.
+            if ((r & (kRowsPerSched<M> - 1)) == kRowsPerSched<M> - 1) order_fence<CW>(cacc, V);
         }
         // Scale guard.  After cycle 1 every row/column factor lies in
         // [1/M, M], so checking every 4th cycle against 2^+-40 keeps P V U,
@@ -326,15 +381,15 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         bool bad = false;
         if constexpr (L == 1) {
 #pragma unroll
-            for (int j = 0; j < M; ++j) V[j] = V[j] * (fN * rcpf(cacc[j]));
+            for (int c = 0; c < CW; ++c) V[c] = V[c] * (fN * rcpf(cacc[c]));
             if ((it & 3) == 0) {
                 float lo = V[0], hi = V[0];
 #pragma unroll
-                for (int j = 1; j < M; ++j) { lo = fminf(lo, V[j]); hi = fmaxf(hi, V[j]); }
+                for (int c = 1; c < CW; ++c) { lo = fminf(lo, V[c]); hi = fmaxf(hi, V[c]); }
                 bad = !(lo >= 0x1p-40f && hi <= 0x1p40f);
             }
         } else {
-            bad = col_exchange<M, 1, false>(cacc, V, lds, blk, k, fN);
+            bad = col_exchange<M, 1, false>(cacc, V, lds, blk, lb, fN);
         }
         if ((it & 3) != 0) continue;
 #pragma unroll
@@ -351,17 +406,20 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                 for (int r = 0; r < R; ++r) {
                     const float u = fN * rcpf(rho[r] * fN);
 #pragma unroll
-                    for (int j = 0; j < M; ++j) P[r][j] = (P[r][j] * V[j]) * u;
+                    for (int c = 0; c < CW; ++c) P[r][c] = (P[r][c] * V[c]) * u;
                 }
 #pragma unroll
-                for (int j = 0; j < M; ++j) V[j] = 1.f;
+                for (int c = 0; c < CW; ++c) V[c] = 1.f;
 #pragma unroll
                 for (int r = 0; r < R; ++r) rho[r] = 1.f;
             }
             if constexpr (L > 1) {
-                float* bcr = lds + kBcastOff<M> + blk * kPadRow<M>;
+                float* bcr = lds + kBcastOff<M> + blk * kRowStride<M>;
                 __syncthreads();
-                if (f) *reinterpret_cast<float4*>(bcr + 4 * k) = make_float4(1.f, 1.f, 1.f, 1.f);
+                if (f) {
+#pragma unroll
+                    for (int c = 0; c < kCPL<M>; ++c) bcr[lb * kCPL<M> + c] = 1.f;
+                }
                 __syncthreads();
             }
         }
@@ -373,24 +431,24 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     for (int r = 0; r < R; ++r) {
         // U_i = N / R_i of the last C1 = N / (rho_i N); 1 on a one-cycle run
         const float u = (prm.iters > 1) ? fN * rcpf(rho[r] * fN) : 1.0f;
-        float s[M];
+        float s[CW];
 #pragma unroll
-        for (int j = 0; j < M; ++j) s[j] = fminf((P[r][j] * V[j]) * u, 1.0f);
-        float* srow = slot + blk * M * M + (k * R + r) * M;
+        for (int c = 0; c < CW; ++c) s[c] = fminf((P[r][c] * V[c]) * u, 1.0f);
+        float* srow = slot + blk * M * M + (g * R + r) * M + h * CW;
 #pragma unroll
-        for (int q = 0; q < M / 4; ++q)
+        for (int q = 0; q < CW / 4; ++q)
             *reinterpret_cast<float4*>(srow + 4 * q) =
                 make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
         if (job.frac != nullptr && valid) {
-            float* frow = job.frac + (br * M + k * R + r) * job.cols + bc * M;
+            float* frow = job.frac + (row0 + r) * job.cols + col0;
             if (fvec) {
 #pragma unroll
-                for (int q = 0; q < M / 4; ++q)
+                for (int q = 0; q < CW / 4; ++q)
                     *reinterpret_cast<float4*>(frow + 4 * q) =
                         make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
             } else {
 #pragma unroll
-                for (int j = 0; j < M; ++j) frow[j] = s[j];
+                for (int c = 0; c < CW; ++c) frow[c] = s[c];
             }
         }
     }
@@ -516,26 +574,33 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
                                            int ls_steps, float* __restrict__ lds) {
     constexpr int G = kWave / M;
     constexpr uint32_t FULL = kFull<M>;
-    const int lane = threadIdx.x;
+    int lane = threadIdx.x;
+    // Opaque to the optimiser: nothing derived from the lane (per-entry key
+    // bits, LDS addresses) is hoisted out of the surrounding loops, where it
+    // would stay live -- and cost registers -- through the solve.
+    asm volatile("" : "+v"(lane));
     const int q = lane / M, i = lane % M;
     const int N = job.N;
 
     // Stage the pass's blocks in LDS (row stride M+1: column reads are
     // conflict-free), then sort row i and column i by key and keep only the
     // bit of each sorted entry.
-    float* Ss = lds;  // [G][M][M+1]
+    float* Ss = lds;  // [G] blocks of [M][M+4]
     {
         float v[M];
         load_row_f32<M>(Sb + i * sld, (reinterpret_cast<uintptr_t>(Sb) & 15u) == 0 && (sld & 3) == 0, v);
-        float* dst = Ss + (q * M + i) * (M + 1);
+        float* dst = Ss + q * kStageBlk<M> + i * kStageRow<M>;
 #pragma unroll
-        for (int j = 0; j < M; ++j) dst[j] = valid ? v[j] : 0.f;
+        for (int k4 = 0; k4 < M / 4; ++k4)
+            *reinterpret_cast<float4*>(dst + 4 * k4) =
+                valid ? make_float4(v[4 * k4], v[4 * k4 + 1], v[4 * k4 + 2], v[4 * k4 + 3])
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
     uint32_t rpb[M], cpb[M];
     {
         double key[M];
-        const float* src = Ss + (q * M + i) * (M + 1);
+        const float* src = Ss + q * kStageBlk<M> + i * kStageRow<M>;
 #pragma unroll
         for (int j = 0; j < M; ++j) key[j] = make_key<M>(src[j], i * M + j);
         sort_desc<M>(key);
@@ -548,9 +613,9 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     __builtin_amdgcn_sched_barrier(0);
     {
         double key[M];
-        const float* src = Ss + q * M * (M + 1) + i;
+        const float* src = Ss + q * kStageBlk<M> + i;
 #pragma unroll
-        for (int r = 0; r < M; ++r) key[r] = make_key<M>(src[r * (M + 1)], r * M + i);
+        for (int r = 0; r < M; ++r) key[r] = make_key<M>(src[r * kStageRow<M>], r * M + i);
         sort_desc<M>(key);
 #pragma unroll
         for (int k = 0; k < M; ++k) {
@@ -704,7 +769,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
 template <int M, bool BF16>
 __device__ __forceinline__ void process_group(const MatJob& job, const Params& prm, int64_t gl,
                                               float* slot, float* lds) {
-    constexpr int BPG = Geo<M>::BPG, G = kWave / M;
+    constexpr int BPG = kBPG<M>, G = kWave / M;
     const int64_t nbc = job.cols / M;
     const int64_t gpr = (nbc + BPG - 1) / BPG;
     const int64_t br = gl / gpr, bc0 = (gl % gpr) * BPG;
@@ -722,7 +787,7 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
 template <int M, bool BF16>
 __global__ __launch_bounds__(kWave) void mask_kernel(MatJob job, Params prm) {
     __shared__ __attribute__((aligned(16))) float lds[lds_floats<M>()];
-    constexpr int BPG = Geo<M>::BPG;
+    constexpr int BPG = kBPG<M>;
     const int64_t nbc = job.cols / M;
     const int64_t ngroups = (job.rows / M) * ((nbc + BPG - 1) / BPG);
     float* slot = prm.scratch + (int64_t)blockIdx.x * kSlotFloats;
@@ -791,6 +856,19 @@ __global__ __launch_bounds__(kWave) void batched_kernel(const MatJob* __restrict
             default: return (int)hipErrorInvalidValue;                  \
         }                                                               \
     } while (0)
+
+int blocks_per_group(int M) {
+    static_assert(kBPG<4> * 16 <= kSlotFloats && kBPG<8> * 64 <= kSlotFloats &&
+                      kBPG<16> * 256 <= kSlotFloats && kBPG<32> * 1024 <= kSlotFloats,
+                  "a group's S fits one workspace slot");
+    switch (M) {
+        case 4: return kBPG<4>;
+        case 8: return kBPG<8>;
+        case 16: return kBPG<16>;
+        case 32: return kBPG<32>;
+        default: return 0;
+    }
+}
 
 int launch_mask(const MatJob& job, const Params& prm, int grid, void* stream) {
     TSENOR_DISPATCH(job.M, job.bf16,
