@@ -64,7 +64,6 @@ template <int M> constexpr int kG = M / kR<M>;           // row groups per block
 template <int M> constexpr int kL = kG<M> * kH<M>;       // lanes per block
 template <int M> constexpr int kBPG = kWave / kL<M>;     // blocks per group
 template <int M> constexpr int kCPL = M / kL<M>;         // columns finalised per lane
-template <int M> constexpr int kRowsPerSched = 1;        // rows scheduled together in the loop
 static_assert(kBPG<32> * 32 % 32 == 0 && kBPG<16> * 16 % 32 == 0, "groups cover whole words");
 
 template <int M> constexpr int kRowStride = M + 4;                      // floats per partial row
@@ -169,11 +168,11 @@ __device__ __forceinline__ float tree_sum(const float (&v)[M]) {
 template <int H, bool MAXOP>
 __device__ __forceinline__ float row_allreduce(float x) {
     if constexpr (H >= 2) {
-        const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-        x = MAXOP ? fmaxf(x, y) : x + y;  // quad_perm [1,0,3,2]: lane ^ 1
+        const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+        x = MAXOP ? fmaxf(x, y) : x + y;  // quad_perm [1,0,3,2]: lane ^ 1 (all lanes active)
     }
     if constexpr (H >= 4) {
-        const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+        const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
         x = MAXOP ? fmaxf(x, y) : x + y;  // quad_perm [2,3,0,1]: lane ^ 2
     }
     static_assert(H == 1 || H == 2 || H == 4, "H");
@@ -242,6 +241,20 @@ __device__ __forceinline__ void order_fence(float (&a)[CW], float (&b)[CW]) {
     for (int c = 0; c < CW; c += 4)
         asm volatile("" : "+v"(a[c]), "+v"(a[c + 1]), "+v"(a[c + 2]), "+v"(a[c + 3]),
                           "+v"(b[c]), "+v"(b[c + 1]), "+v"(b[c + 2]), "+v"(b[c + 3]));
+}
+
+// Clipped products of one tile row: t_c = min(P_c V_c, rho); returns their
+// sum in a fixed order (four interleaved partial sums, then pairwise).
+template <int CW>
+__device__ __forceinline__ float row_products(const float (&Pr)[CW], const float (&V)[CW], float rho,
+                                              float (&t)[CW]) {
+    float acc[4];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
+        t[c] = fminf(Pr[c] * V[c], rho);
+        acc[c & 3] = (c < 4) ? t[c] : acc[c & 3] + t[c];
+    }
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // ---------------------------------------------------------------- solve
@@ -353,27 +366,27 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         // made visible by the first exchange's barrier
     }
     for (int it = 1; it < prm.iters; ++it) {
-        float cacc[CW];
+        // Rows are software-pipelined: each fenced region finishes row r (sum
+        // across the H lanes, reciprocal, column FMAs) while it computes row
+        // r+1's clipped products, which hides the latency of the row tail.
+        float cacc[CW], tc[CW], tn[CW];
+        float pc = row_products<CW>(P[0], V, rho[0], tc), pn = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float t[CW];
-            float acc[4];
-#pragma unroll
-            for (int c = 0; c < CW; ++c) {
-                t[c] = fminf(P[r][c] * V[c], rho[r]);
-                acc[c & 3] = (c < 4) ? t[c] : acc[c & 3] + t[c];
-            }
-            const float rs = row_allreduce<H, false>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+            const float rs = row_allreduce<H, false>(pc);
             const float u = fN * rcpf(rs);
             rho[r] = rs * invN;
+            if (r + 1 < R) pn = row_products<CW>(P[r + 1 < R ? r + 1 : 0], V, rho[r + 1 < R ? r + 1 : 0], tn);
 #pragma unroll
-            for (int c = 0; c < CW; ++c) cacc[c] = (r == 0) ? t[c] * u : fmaf(t[c], u, cacc[c]);
-            // Keep one row's temporaries live at a time: left alone, the
-            // instruction selector hoists every row's products and spills the
-            // tile.  The empty asm claims to update cacc and V, so this row's
-            // column updates complete before, and the next row's products
-            // start after, this point.  No instruction is emitted.
-            if ((r & (kRowsPerSched<M> - 1)) == kRowsPerSched<M> - 1) order_fence<CW>(cacc, V);
+            for (int c = 0; c < CW; ++c) cacc[c] = (r == 0) ? tc[c] * u : fmaf(tc[c], u, cacc[c]);
+            // The empty asm claims to update cacc and V, so row r's column
+            // updates complete before, and row r+2's products start after,
+            // this point: one row's temporaries in flight, no spills.  No
+            // instruction is emitted.
+            order_fence<CW>(cacc, V);
+#pragma unroll
+            for (int c = 0; c < CW; ++c) tc[c] = tn[c];
+            pc = pn;
         }
         // Scale guard.  After cycle 1 every row/column factor lies in
         // [1/M, M], so checking every 4th cycle against 2^+-40 keeps P V U,
