@@ -90,6 +90,12 @@ __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x);
 __device__ __forceinline__ float rcpf(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // ---------------------------------------------------------------- gather
+// Native vector types for the streaming (non-temporal) loads of W: the
+// weights are read once and should not evict the workspace slots from L2.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // |W| of M consecutive elements starting at element offset `off`, as fp32.
 template <int M, bool BF16>
 __device__ __forceinline__ void load_abs_row(const void* W, int64_t off, bool vec, float (&out)[M]) {
@@ -99,7 +105,7 @@ __device__ __forceinline__ void load_abs_row(const void* W, int64_t off, bool ve
             if constexpr (M >= 8) {
 #pragma unroll
                 for (int q = 0; q < M / 8; ++q) {
-                    const uint4 v = reinterpret_cast<const uint4*>(p)[q];
+                    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + q);
                     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
@@ -108,7 +114,7 @@ __device__ __forceinline__ void load_abs_row(const void* W, int64_t off, bool ve
                     }
                 }
             } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(p);
+                const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
                 out[0] = __uint_as_float((v.x & 0x7FFFu) << 16);
                 out[1] = __uint_as_float(v.x & 0x7FFF0000u);
                 out[2] = __uint_as_float((v.y & 0x7FFFu) << 16);
@@ -123,7 +129,7 @@ __device__ __forceinline__ void load_abs_row(const void* W, int64_t off, bool ve
         if (vec) {
 #pragma unroll
             for (int q = 0; q < M / 4; ++q) {
-                const float4 v = reinterpret_cast<const float4*>(p)[q];
+                const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + q);
                 out[4 * q] = fabsf(v.x);
                 out[4 * q + 1] = fabsf(v.y);
                 out[4 * q + 2] = fabsf(v.z);
@@ -474,9 +480,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 // Larger key = earlier in (s descending, idx ascending).
 template <int M>
 __device__ __forceinline__ double make_key(float s, int idx) {
-    uint32_t u = __float_as_uint(s);
-    if (u == 0x80000000u) u = 0u;  // -0 -> +0
-    const double d = (double)__uint_as_float(u);
+    const double d = (double)(s + 0.0f);  // -0 -> +0
     const uint64_t b = ((uint64_t)__double_as_longlong(d) + (1ull << 52)) |
                        (uint64_t)(M * M - 1 - idx);
     return __longlong_as_double((long long)b);
@@ -486,25 +490,26 @@ __device__ __forceinline__ int key_index(double key) {
     return M * M - 1 - (int)((uint32_t)__double_as_longlong(key) & (uint32_t)(M * M - 1));
 }
 
-// Bitonic network, descending, on registers.
+// Batcher's odd-even merge sort network (descending) on registers: 191
+// compare-exchanges for 32 keys (bitonic needs 240).  Every index is a
+// compile-time constant after unrolling.
 template <int M>
 __device__ __forceinline__ void sort_desc(double (&a)[M]) {
 #pragma unroll
-    for (int size = 2; size <= M; size <<= 1)
+    for (int p = 1; p < M; p <<= 1)
 #pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1)
+        for (int k = p; k >= 1; k >>= 1)
 #pragma unroll
-            for (int x = 0; x < M; ++x) {
-                const int y = x ^ stride;
-                if (y > x) {
-                    const double hi = fmax(a[x], a[y]), lo = fmin(a[x], a[y]);
-                    if ((x & size) == 0) {
-                        a[x] = hi; a[y] = lo;
-                    } else {
-                        a[x] = lo; a[y] = hi;
+            for (int j = k % p; j + k < M; j += 2 * k)
+#pragma unroll
+                for (int i = 0; i < k; ++i) {
+                    const int x = i + j, y = i + j + k;
+                    if (y < M && x / (2 * p) == y / (2 * p)) {
+                        const double hi = fmax(a[x], a[y]), lo = fmin(a[x], a[y]);
+                        a[x] = hi;
+                        a[y] = lo;
                     }
                 }
-            }
 }
 
 // Walk a sorted row (or column); pb[k] = bit of the entry at sorted position
@@ -524,6 +529,22 @@ __device__ __forceinline__ uint32_t walk(const uint32_t (&pb)[M], uint32_t allow
     return cnt < N ? kFull<M> : m;
 }
 
+// Same walk for a compile-time N: the first N positions always lie inside
+// the prefix (fewer than N allowed entries precede any of them), so their
+// bits are pre-ORed into `head` and only positions N..M-1 are walked.
+template <int M, int N>
+__device__ __forceinline__ uint32_t walk_tail(uint32_t head, const uint32_t (&tail)[M - N],
+                                              uint32_t allowed) {
+    int cnt = __popc(allowed & head);
+    uint32_t m = head;
+#pragma unroll
+    for (int k = 0; k < M - N; ++k) {
+        m |= (cnt < N) ? tail[k] : 0u;
+        cnt += (allowed & tail[k]) != 0u ? 1 : 0;
+    }
+    return cnt < N ? kFull<M> : m;
+}
+
 __device__ __forceinline__ constexpr uint32_t lowmask(int s) {
     return s == 16 ? 0x0000FFFFu
          : s == 8  ? 0x00FF00FFu
@@ -532,23 +553,48 @@ __device__ __forceinline__ constexpr uint32_t lowmask(int s) {
                    : 0x55555555u;
 }
 
+// Value of x in lane (lane ^ S), by DPP / permlane (no LDS traffic).
+template <int S>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x) {
+    if constexpr (S == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
+    if constexpr (S == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
+    if constexpr (S == 4)  // row_half_mirror then quad_perm [3,2,1,0]
+        return (uint32_t)__builtin_amdgcn_mov_dpp(
+            __builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, true), 0x1B, 0xF, 0xF, true);
+    if constexpr (S == 8) return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, true);  // row_ror:8
+    if constexpr (S == 16) {
+        // permlane16_swap(x, x): result[0] holds lanes 0-15's x in lanes 16-31,
+        // result[1] holds lanes 16-31's x in lanes 0-15.
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (threadIdx.x & 16u) ? r[0] : r[1];
+    }
+    static_assert(S == 1 || S == 2 || S == 4 || S == 8 || S == 16, "xor distance");
+    return x;
+}
+
 // Transpose of the M x M bit matrix held by each aligned group of M lanes
 // (lane i: row i, bit j = column j) -> lane j gets column j (bit i = row i).
+// Level s swaps the off-diagonal s x s sub-blocks between lanes i and i^s:
+// the lower lane keeps its bits with (pos & s) == 0 and takes the partner's
+// low-half bits rotated up by s; the upper lane the mirror image.  A rotation
+// by s moves exactly those bits into place (no bit wraps into a kept
+// position), so each level is one cross-lane move, one alignbit and one bfi.
+template <int M, int S>
+__device__ __forceinline__ uint32_t transpose_level(uint32_t x, uint32_t lane) {
+    const uint32_t up = 0u - ((lane >> __builtin_ctz(S)) & 1u);
+    const uint32_t keep = (lowmask(S) ^ up);            // own bits that stay
+    const uint32_t y = xor_lane<S>(x);
+    const uint32_t rot = __builtin_amdgcn_alignbit(y, y, up ? S : 32 - S);  // rotr(y, .)
+    return (keep & x) | (~keep & rot & kFull<M>);
+}
+
 template <int M>
-__device__ __forceinline__ uint32_t transpose_bits(uint32_t x) {
-    const uint32_t lane = threadIdx.x;
-#pragma unroll
-    for (int s = M / 2; s >= 1; s >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)x, s);
-        const uint32_t lo = lowmask(s) & kFull<M>;
-        const uint32_t up = 0u - ((lane >> __builtin_ctz(s)) & 1u);  // all ones on the upper lane
-        // lower lane: keep own low half, take partner's low half into the high half;
-        // upper lane: keep own high half, take partner's high half into the low half.
-        const uint32_t keep = x & (lo ^ up);
-        const uint32_t take = (y & (lo ^ up));
-        x = keep | (((take << s) & ~up) | ((take >> s) & up));
-    }
-    return x;
+__device__ __forceinline__ uint32_t transpose_bits(uint32_t x, uint32_t lane) {
+    if constexpr (M >= 32) x = transpose_level<M, 16>(x, lane);
+    if constexpr (M >= 16) x = transpose_level<M, 8>(x, lane);
+    if constexpr (M >= 8) x = transpose_level<M, 4>(x, lane);
+    if constexpr (M >= 4) x = transpose_level<M, 2>(x, lane);
+    return transpose_level<M, 1>(x, lane);
 }
 
 __device__ __forceinline__ uint32_t float_to_ord(float f) {
@@ -577,6 +623,46 @@ __device__ __forceinline__ int group_sum(int v) {
 #pragma unroll
     for (int s = 1; s < M; s <<= 1) v += __shfl_xor(v, s);
     return v;
+}
+
+// Greedy over the (S desc, index asc) order, as the fixed point of the row
+// and column thresholds; returns row i of the accepted mask.
+// Row step: Rmask_i = {j : key_ij >= phi_i}, phi_i = N-th largest key of row i
+// among j in Amask_i.  Column step: Cmask_j = {i : key_ij >= theta_j}, theta_j
+// = N-th largest key of column j among i with key_ij >= phi_i.  Amask_i =
+// {j : key_ij >= theta_j}.  Accepted = Rmask & Amask at the fixed point.  The
+// theta sequence rises monotonically from "minus infinity" and can change at
+// most M*M + M times, so the loop bound is never the exit in exact terms.
+// NS > 0: N is the compile-time NS (walks skip the first NS positions).
+template <int M, int NS>
+__device__ __forceinline__ uint32_t greedy_rows(const uint32_t (&rpb)[M], const uint32_t (&cpb)[M],
+                                                int N, uint32_t lane) {
+    uint32_t Amask = kFull<M>, Rmask = kFull<M>, Cmask = 0u;
+    if constexpr (NS > 0) {
+        uint32_t rh = 0u, ch = 0u, rt[M - NS], ct[M - NS];
+#pragma unroll
+        for (int k = 0; k < NS; ++k) { rh |= rpb[k]; ch |= cpb[k]; }
+#pragma unroll
+        for (int k = 0; k < M - NS; ++k) { rt[k] = rpb[NS + k]; ct[k] = cpb[NS + k]; }
+        for (int round = 0; round <= M * M + M + 2; ++round) {
+            Rmask = walk_tail<M, NS>(rh, rt, Amask);
+            const uint32_t Cnew = walk_tail<M, NS>(ch, ct, transpose_bits<M>(Rmask, lane));
+            const bool changed = Cnew != Cmask;
+            Cmask = Cnew;
+            Amask = transpose_bits<M>(Cmask, lane);
+            if (__ballot(changed) == 0ull) break;
+        }
+    } else {
+        for (int round = 0; round <= M * M + M + 2; ++round) {
+            Rmask = walk<M>(rpb, Amask, N);
+            const uint32_t Cnew = walk<M>(cpb, transpose_bits<M>(Rmask, lane), N);
+            const bool changed = Cnew != Cmask;
+            Cmask = Cnew;
+            Amask = transpose_bits<M>(Cmask, lane);
+            if (__ballot(changed) == 0ull) break;
+        }
+    }
+    return Rmask & Amask;
 }
 
 // Rounding of the 64/M blocks handled by this pass: lane (q, i) = block q,
@@ -640,24 +726,12 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     __syncthreads();  // Ss is reused below
 
     // ---- greedy as the fixed point of the row / column thresholds ----
-    // Row step: Rmask_i = {j : key_ij >= phi_i}, phi_i = N-th largest key of
-    // row i among j in Amask_i.  Column step: Cmask_j = {i : key_ij >= theta_j},
-    // theta_j = N-th largest key of column j among i with key_ij >= phi_i.
-    // Amask_i = {j : key_ij >= theta_j}.  The theta sequence rises
-    // monotonically from "minus infinity" and can change at most M*M + M
-    // times, so the loop bound is never the exit in exact terms.
-    uint32_t Amask = FULL, Rmask = FULL, Cmask = 0u;
-    for (int round = 0; round <= M * M + M + 2; ++round) {
-        Rmask = walk<M>(rpb, Amask, N);
-        const uint32_t Cnew = walk<M>(cpb, transpose_bits<M>(Rmask), N);
-        const bool changed = Cnew != Cmask;
-        Cmask = Cnew;
-        Amask = transpose_bits<M>(Cmask);
-        if (__ballot(changed) == 0ull) break;
-    }
-    uint32_t Z = Rmask & Amask;  // row i of the greedy mask
+    const uint32_t ulane = (uint32_t)lane;
+    const uint32_t Z0 = (N == M / 2) ? greedy_rows<M, M / 2>(rpb, cpb, N, ulane)
+                                     : greedy_rows<M, 0>(rpb, cpb, N, ulane);
+    uint32_t Z = Z0;  // row i of the greedy mask
     int r = __popc(Z);
-    int c = __popc(transpose_bits<M>(Z));  // column i count
+    int c = __popc(transpose_bits<M>(Z, ulane));  // column i count
     const int shift = q * M;
     uint32_t DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
     uint32_t DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
@@ -669,7 +743,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
         float* As = lds;                                                   // [G][M][M+1]
         uint32_t* Zs = reinterpret_cast<uint32_t*>(lds + G * M * (M + 1));  // [G][M]
         float arow[M];
-        if (valid) {
+        if (need) {  // only blocks with a shortfall read their |W| again
             load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, arow);
         } else {
 #pragma unroll
