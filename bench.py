@@ -22,10 +22,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "Gweights/s masked (16:32, 8192×28672) + % of VALU/exp roofline"
 PEAK_HBM_GBS = 8000.0
-# fp32 VALU lane-operations per second: 256 CUs x 64 lanes x 2.4 GHz (packed
-# fp32 issue is not used by these kernels).
-PEAK_VALU_TOPS = 256 * 64 * 2.4e9 / 1e12
-OPS_PER_ELEM_ITER = 4  # P*V (mul), clip (min), row sum (add), column sum (fma)
+# fp32 VALU lane-operations per second: 256 CUs x 4 SIMDs x 32 fp32 lanes per
+# clock (a wave64 fp32 op retires in 2 clocks on one SIMD) x 2.4 GHz = 78.6 T
+# (the vector-fp32 peak of 157.3 TFLOP/s counts an FMA as two).
+PEAK_VALU_TOPS = 256 * 128 * 2.4e9 / 1e12
+# per element and Dykstra cycle: P*V (mul), *U with clamp to [0,1] (the clip),
+# row sum (add), column sum (fma)
+OPS_PER_ELEM_ITER = 4
 
 
 def log(*a):

@@ -16,12 +16,13 @@
 //              rows and columns, robust for any tau); every later cycle in
 //              scaling form.  With Y = X + Q the cycle is Y += a_i + b_j and
 //              X = min(Y, 0), so keeping P = 2^Y (fixed after cycle 1), a row
-//              scale U_i = 1/rho_i and a column scale V_j, one cycle is
-//                 t_ij = min(P_ij V_j, rho_i)     (= exp(X_ij) * rho_i)
-//                 R_i  = sum_j t_ij,  U_i = N/R_i,  rho_i = R_i/N      (C1)
-//                 C_j  = sum_i t_ij U_i,  V_j *= N/C_j          (C2, C3 implicit)
-//              i.e. 4 fp32 VALU ops per element and no transcendental per
-//              element.  Rows live in lanes; column sums of blocks spread over
+//              scale U_i and a column scale V_j, one cycle is
+//                 E_ij = min(P_ij V_j U_i, 1)     (= exp(X_ij))          (C3)
+//                 a_i  = N / sum_j E_ij,           U_i *= a_i            (C1)
+//                 b_j  = N / sum_i E_ij a_i,       V_j *= b_j            (C2)
+//              i.e. 4 full-rate fp32 VALU ops per element -- mul, mul with
+//              the clamp output modifier (the clip; v_min is half rate on
+//              this chip), add, fma -- and no transcendental per element.  Rows live in lanes; column sums of blocks spread over
 //              several lanes are reduced through LDS (reduce-scatter, then a
 //              broadcast of the new V).
 //  3. export   S = min(P V U, 1) is written to the workgroup's scratch slot
@@ -249,20 +250,6 @@ __device__ __forceinline__ void order_fence(float (&a)[CW], float (&b)[CW]) {
                           "+v"(b[c]), "+v"(b[c + 1]), "+v"(b[c + 2]), "+v"(b[c + 3]));
 }
 
-// Clipped products of one tile row: t_c = min(P_c V_c, rho); returns their
-// sum in a fixed order (four interleaved partial sums, then pairwise).
-template <int CW>
-__device__ __forceinline__ float row_products(const float (&Pr)[CW], const float (&V)[CW], float rho,
-                                              float (&t)[CW]) {
-    float acc[4];
-#pragma unroll
-    for (int c = 0; c < CW; ++c) {
-        t[c] = fminf(Pr[c] * V[c], rho);
-        acc[c & 3] = (c < 4) ? t[c] : acc[c & 3] + t[c];
-    }
-    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
-}
-
 // ---------------------------------------------------------------- solve
 // Dykstra for the group's blocks; writes S (fp32) for block b of the group to
 // slot[b*M*M ...] row-major, and to job.frac when requested.
@@ -278,7 +265,6 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     const int64_t bc = bc0 + blk;
     const bool valid = bc < nbc;
     const float fN = (float)job.N;
-    const float invN = 1.0f / fN;
     const float log2N = log2f(fN);
     const bool vec = job.aligned != 0;
     const int64_t row0 = br * M + g * R;      // first matrix row of this lane's tile
@@ -360,11 +346,11 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     }
 
     // ---- cycles 2..T in scaling form ----
-    float V[CW], rho[R];
+    float V[CW], U[R];
 #pragma unroll
     for (int c = 0; c < CW; ++c) V[c] = 1.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) rho[r] = 1.f;
+    for (int r = 0; r < R; ++r) U[r] = 1.f;
     if constexpr (L > 1) {
         float* bcr = lds + kBcastOff<M> + blk * kRowStride<M>;
 #pragma unroll
@@ -372,31 +358,31 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         // made visible by the first exchange's barrier
     }
     for (int it = 1; it < prm.iters; ++it) {
-        // Rows are software-pipelined: each fenced region finishes row r (sum
-        // across the H lanes, reciprocal, column FMAs) while it computes row
-        // r+1's clipped products, which hides the latency of the row tail.
-        float cacc[CW], tc[CW], tn[CW];
-        float pc = row_products<CW>(P[0], V, rho[0], tc), pn = 0.f;
+        float cacc[CW];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float rs = row_allreduce<H, false>(pc);
-            const float u = fN * rcpf(rs);
-            rho[r] = rs * invN;
-            if (r + 1 < R) pn = row_products<CW>(P[r + 1 < R ? r + 1 : 0], V, rho[r + 1 < R ? r + 1 : 0], tn);
+            float e[CW], acc[4];
 #pragma unroll
-            for (int c = 0; c < CW; ++c) cacc[c] = (r == 0) ? tc[c] * u : fmaf(tc[c], u, cacc[c]);
-            // The empty asm claims to update cacc and V, so row r's column
-            // updates complete before, and row r+2's products start after,
-            // this point: one row's temporaries in flight, no spills.  No
-            // instruction is emitted.
+            for (int c = 0; c < CW; ++c) {
+                // E = min(P V U, 1): the clamp folds into the second multiply
+                e[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
+                acc[c & 3] = (c < 4) ? e[c] : acc[c & 3] + e[c];
+            }
+            const float rs = row_allreduce<H, false>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+            const float a = fN * rcpf(rs);
+            U[r] *= a;
+#pragma unroll
+            for (int c = 0; c < CW; ++c) cacc[c] = (r == 0) ? e[c] * a : fmaf(e[c], a, cacc[c]);
+            // Keep one row's temporaries live at a time: left alone, the
+            // instruction selector hoists every row's products and spills the
+            // tile.  The empty asm claims to update cacc and V, so this row's
+            // column updates complete before, and the next row's products
+            // start after, this point.  No instruction is emitted.
             order_fence<CW>(cacc, V);
-#pragma unroll
-            for (int c = 0; c < CW; ++c) tc[c] = tn[c];
-            pc = pn;
         }
         // Scale guard.  After cycle 1 every row/column factor lies in
         // [1/M, M], so checking every 4th cycle against 2^+-40 keeps P V U,
-        // rho and V far inside the fp32 range.
+        // U and V far inside the fp32 range.
         bool bad = false;
         if constexpr (L == 1) {
 #pragma unroll
@@ -412,7 +398,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         }
         if ((it & 3) != 0) continue;
 #pragma unroll
-        for (int r = 0; r < R; ++r) bad |= !(rho[r] >= 0x1p-40f && rho[r] <= 0x1p40f);
+        for (int r = 0; r < R; ++r) bad |= !(U[r] >= 0x1p-40f && U[r] <= 0x1p40f);
         bad = bad && valid;
         if (__builtin_expect(__ballot(bad) != 0ull, 0)) {
             // Rare: fold the scales into P (P <- P V U, scales <- 1) so that
@@ -422,15 +408,13 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             for (int s = 1; s < L; s <<= 1) f |= __shfl_xor(f, s);
             if (f) {
 #pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const float u = fN * rcpf(rho[r] * fN);
+                for (int r = 0; r < R; ++r)
 #pragma unroll
-                    for (int c = 0; c < CW; ++c) P[r][c] = (P[r][c] * V[c]) * u;
-                }
+                    for (int c = 0; c < CW; ++c) P[r][c] = (P[r][c] * V[c]) * U[r];
 #pragma unroll
                 for (int c = 0; c < CW; ++c) V[c] = 1.f;
 #pragma unroll
-                for (int r = 0; r < R; ++r) rho[r] = 1.f;
+                for (int r = 0; r < R; ++r) U[r] = 1.f;
             }
             if constexpr (L > 1) {
                 float* bcr = lds + kBcastOff<M> + blk * kRowStride<M>;
@@ -448,11 +432,9 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     const bool fvec = ((reinterpret_cast<uintptr_t>(job.frac) & 15u) == 0);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        // U_i = N / R_i of the last C1 = N / (rho_i N); 1 on a one-cycle run
-        const float u = (prm.iters > 1) ? fN * rcpf(rho[r] * fN) : 1.0f;
         float s[CW];
 #pragma unroll
-        for (int c = 0; c < CW; ++c) s[c] = fminf((P[r][c] * V[c]) * u, 1.0f);
+        for (int c = 0; c < CW; ++c) s[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
         float* srow = slot + blk * M * M + (g * R + r) * M + h * CW;
 #pragma unroll
         for (int q = 0; q < CW / 4; ++q)
