@@ -7,6 +7,11 @@ steps -- the configuration the headline metric is quoted on.  One "step" is
 one tsenor_mask call: gather, Dykstra, rounding (greedy, local search, fill)
 and the bit-packed mask write over the whole matrix, inputs resident in HBM.
 
+`--workload 7b-model-batched` times instead one tsenor_mask_batched call over
+the 224 projections of a 32-layer 7B-shaped model (8:16 on q/k/v/o 4096x4096,
+16:32 on gate/up 4096x11008 and down 11008x4096; tau 30, 150 iterations,
+16 steps; 6.48 G weights, 12.1 GiB of bf16 resident on the GPU).
+
 Prints ONE JSON line on stdout; progress goes to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -61,6 +66,130 @@ def cpu_baseline(w, W_np, seconds):
                       f"{k * (w.cols // w.M)} blocks, {t:.1f} s"}
 
 
+MODEL7B = "7b-model-batched"
+
+
+def _gen_layer(layer):
+    from sparse_mask_search_amd import workloads as wl
+    return layer, [(nm, N, M, W) for nm, N, M, W in wl.model7b_layer(layer)]
+
+
+def model7b_resident():
+    """Every projection of the 7B-shaped model as bf16 CUDA tensors, generated
+    on the host in parallel (one seeded generator per layer)."""
+    import multiprocessing as mp
+
+    import numpy as np
+    import torch
+
+    from sparse_mask_search_amd import workloads as wl
+    mats = [None] * wl.MODEL7B_LAYERS
+    workers = max(1, min(8, (os.cpu_count() or 1)))
+    with mp.get_context("spawn").Pool(workers) as pool:
+        for layer, items in pool.imap_unordered(_gen_layer, range(wl.MODEL7B_LAYERS)):
+            mats[layer] = [(torch.from_numpy(W.view(np.int16)).cuda().view(torch.bfloat16), N, M, nm)
+                           for nm, N, M, W in items]
+            log(f"[bench] layer {layer} resident")
+    return [m for layer in mats for m in layer]
+
+
+def cpu_baseline_7b(seconds):
+    """The oracle on the first block-rows of every projection of layer 0; the
+    rate is extrapolated to the model's mix of 8:16 and 16:32 weights."""
+    import numpy as np
+
+    import oracle
+    from sparse_mask_search_amd import workloads as wl
+
+    oracle.build(force=False)
+    mats = list(wl.model7b_layer(0))
+    budget = seconds / len(mats)
+    t_model, n_sample, t_sample = 0.0, 0, 0.0
+    for nm, N, M, W in mats:
+        def run(k):
+            Wf = np.ascontiguousarray(wl.bf16_bits_to_f32(W[:k * M]))
+            t0 = time.perf_counter()
+            oracle.tsenor(Wf, N, M, wl.MODEL7B_TAU, wl.MODEL7B_ITERS, wl.MODEL7B_LS)
+            return time.perf_counter() - t0, Wf.size
+        t1, n1 = run(1)
+        k = int(max(1, min(W.shape[0] // M, round(budget / max(t1, 1e-3)))))
+        t, n = run(k) if k > 1 else (t1, n1)
+        t_model += t / n * W.size * wl.MODEL7B_LAYERS
+        n_sample += n
+        t_sample += t
+    weights = sum(W.size for _, _, _, W in mats) * wl.MODEL7B_LAYERS
+    return {"value": weights / t_model / 1e9, "unit": "Gweights/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"first block-rows of each layer-0 projection: {n_sample} weights in "
+                      f"{t_sample:.1f} s, per-projection rates weighted by the model's weights"}
+
+
+def main_7b(args):
+    import numpy as np
+    import torch
+
+    import sparse_mask_search_amd as sms
+    from sparse_mask_search_amd import workloads as wl
+
+    t0 = time.perf_counter()
+    mats = model7b_resident()
+    log(f"[bench] 224 matrices resident in {time.perf_counter() - t0:.1f} s")
+    outs = [torch.empty((W.shape[0], W.shape[1] // 32), dtype=torch.int32, device="cuda")
+            for W, _, _, _ in mats]
+    items = [(W, N, M, o) for (W, N, M, _), o in zip(mats, outs)]
+    weights = sum(W.numel() for W, _, _, _ in mats)
+    blocks = sum(W.numel() // (M * M) for W, _, M, _ in mats)
+    elem_iters = weights * (wl.MODEL7B_ITERS - 1)
+
+    def step():
+        sms.mask_batched([(W, N, M) for W, N, M, _ in items], wl.MODEL7B_TAU, wl.MODEL7B_ITERS,
+                         wl.MODEL7B_LS, outs=[o for _, _, _, o in items])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = float(np.mean(kern_ms))
+    ms_wall = wall * 1e3 / args.steps
+    log(f"[bench] ms/step mean {ms:.2f} (min {min(kern_ms):.2f} max {max(kern_ms):.2f}); wall {ms_wall:.2f}")
+    ops = OPS_PER_ELEM_ITER * elem_iters
+    achieved = ops / (ms / 1e3) / 1e12
+    rec = {
+        "metric": "Gweights/s masked (7B-shaped model, 224 projections, one batched call)",
+        "value": round(weights / (ms_wall / 1e3) / 1e9, 4),
+        "unit": "Gweights/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": MODEL7B, "matrices": len(mats), "weights": weights,
+                   "blocks": blocks, "input_dtype": "bf16", "tau": wl.MODEL7B_TAU,
+                   "iters": wl.MODEL7B_ITERS, "ls_steps": wl.MODEL7B_LS,
+                   "recipe": "per layer l: seed 1000+l; q,k,v,o,gate,up,down = 0.02*normal "
+                             "+ 0.1% +-U(0.5,2) outliers, bf16"},
+        "blocks_per_s": round(blocks / (ms_wall / 1e3), 1),
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_VALU_TOPS,
+                     "unit": "Tops/s", "frac": round(achieved / PEAK_VALU_TOPS, 4),
+                     "traffic": None,
+                     "kernel": "batched_kernel (one launch per N:M class)",
+                     "kernel_ms": round(ms, 3), "ops_per_launch": ops},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        rec["cpu_baseline"] = cpu_baseline_7b(args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -74,6 +203,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the method has no "
               "cross-GPU step and this build measures a single MI355X.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == MODEL7B:
+        return main_7b(args)
 
     import numpy as np
     import torch

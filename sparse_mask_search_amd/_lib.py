@@ -88,10 +88,19 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _mask_buffer(W):
+def _mask_buffer(W, out=None):
+    """A fresh mask buffer for W, or `out` after checking that the kernels may
+    write [rows][ceil(cols/32)] contiguous words into it."""
     torch = _torch()
     rows, cols = W.shape
-    return torch.empty((rows, (cols + 31) // 32), dtype=torch.int32, device=W.device)
+    shape = (rows, (cols + 31) // 32)
+    if out is None:
+        return torch.empty(shape, dtype=torch.int32, device=W.device)
+    if (out.dtype != torch.int32 or out.device != W.device or tuple(out.shape) != shape
+            or not out.is_contiguous()):
+        raise ValueError(f"mask buffer must be a contiguous int32 tensor of shape {shape} "
+                         f"on {W.device}")
+    return out
 
 
 def mask(W, N: int, M: int, tau: float, iters: int, ls_steps: int, return_frac: bool = False,
@@ -104,9 +113,14 @@ def mask(W, N: int, M: int, tau: float, iters: int, ls_steps: int, return_frac: 
     torch = _torch()
     dt = _weights(W)
     rows, cols = W.shape
-    out = _mask_buffer(W) if out is None else out
+    out = _mask_buffer(W, out)
     if frac_out is None and return_frac:
         frac_out = torch.empty((rows, cols), dtype=torch.float32, device=W.device)
+    elif frac_out is not None and (frac_out.dtype != torch.float32 or frac_out.device != W.device
+                                   or tuple(frac_out.shape) != (rows, cols)
+                                   or not frac_out.is_contiguous()):
+        raise ValueError(f"frac_out must be a contiguous float32 tensor of shape {(rows, cols)} "
+                         f"on {W.device}")
     st = lib().tsenor_mask(ctypes.c_void_p(W.data_ptr()), dt, rows, cols, W.stride(0), N, M,
                            float(tau), int(iters), int(ls_steps), ctypes.c_void_p(out.data_ptr()),
                            ctypes.c_void_p(frac_out.data_ptr() if frac_out is not None else 0),
@@ -125,7 +139,7 @@ def round_mask(S, W, N: int, M: int, ls_steps: int, out=None, stream=None):
     if tuple(S.shape) != tuple(W.shape):
         raise ValueError("S and W shapes differ")
     rows, cols = W.shape
-    out = _mask_buffer(W) if out is None else out
+    out = _mask_buffer(W, out)
     st = lib().tsenor_round(ctypes.c_void_p(S.data_ptr()), S.stride(0),
                             ctypes.c_void_p(W.data_ptr()), dt, rows, cols, W.stride(0), N, M,
                             int(ls_steps), ctypes.c_void_p(out.data_ptr()), _stream(stream))
@@ -135,26 +149,29 @@ def round_mask(S, W, N: int, M: int, ls_steps: int, out=None, stream=None):
 
 
 def mask_batched(items, tau: float, iters: int, ls_steps: int, return_frac: bool = False,
-                 stream=None):
-    """One launch over many matrices.  items: iterable of (W, N, M).
-    Returns a list of (mask, frac_or_None) in the same order."""
+                 outs=None, stream=None):
+    """Many matrices in one call (one launch per N:M and dtype class).
+    items: iterable of (W, N, M); outs: optional list of mask buffers, one per
+    item.  Returns a list of (mask, frac_or_None) in the same order."""
     torch = _torch()
     items = list(items)
+    if outs is not None and len(outs) != len(items):
+        raise ValueError("outs must hold one mask buffer per item")
     arr = (_Matrix * max(1, len(items)))()
-    outs = []
+    res = []
     for k, (W, N, M) in enumerate(items):
         dt = _weights(W)
         rows, cols = W.shape
-        m = _mask_buffer(W)
+        m = _mask_buffer(W, outs[k] if outs is not None else None)
         f = torch.empty((rows, cols), dtype=torch.float32, device=W.device) if return_frac else None
         arr[k] = _Matrix(W.data_ptr(), dt, rows, cols, W.stride(0), N, M, m.data_ptr(),
                          f.data_ptr() if f is not None else 0)
-        outs.append((m, f))
+        res.append((m, f))
     st = lib().tsenor_mask_batched(arr, len(items), float(tau), int(iters), int(ls_steps),
                                    _stream(stream))
     if st != 0:
         raise TsenorError(st, "tsenor_mask_batched")
-    return outs
+    return res
 
 
 def unpack(mask_words, cols: int):

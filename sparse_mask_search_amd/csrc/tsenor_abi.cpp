@@ -41,7 +41,7 @@ struct DeviceState {
     size_t jobs_cap = 0;
     int occ_mask[2][33] = {};
     int occ_round[2][33] = {};
-    int occ_batched = 0;
+    int occ_batched[2][33] = {};
 };
 DeviceState g_dev[kMaxDevices];
 
@@ -106,8 +106,8 @@ int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
             for (int M : {4, 8, 16, 32}) {
                 st.occ_mask[b][M] = tsenor::occupancy_mask(M, b);
                 st.occ_round[b][M] = tsenor::occupancy_round(M, b);
+                st.occ_batched[b][M] = tsenor::occupancy_batched(M, b);
             }
-        st.occ_batched = tsenor::occupancy_batched();
         st.init = true;
     }
     *out = &st;
@@ -244,16 +244,31 @@ int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int ite
         e = hipEventSynchronize(st->last);
         if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     }
-    int64_t total = 0;
-    for (int i = 0; i < count; ++i) {
-        const tsenor_matrix& m = mats[i];
-        MatJob j = make_job(m.W, m.dtype, m.rows, m.cols, m.ld, m.N, m.M, m.mask_out, m.frac_out);
-        j.group_begin = total;
-        total += groups_of(j);
-        st->jobs_host[i] = j;
-    }
-    const int64_t grid = clamp_grid(total, st->num_cu, st->occ_batched);
-    if ((st_code = ensure_scratch(*st, (size_t)grid)) != TSENOR_OK) return st_code;
+    // One launch per (M, dtype) class present; the class's descriptors are
+    // contiguous in the table, in call order, with group ids counted from 0.
+    struct Class { int M, bf16, first, n; int64_t groups, grid; };
+    Class cls[8];
+    int ncls = 0, filled = 0;
+    int64_t max_grid = 0;
+    for (int M : {32, 16, 8, 4})
+        for (int b = 0; b < 2; ++b) {
+            Class c{M, b, filled, 0, 0, 0};
+            for (int i = 0; i < count; ++i) {
+                const tsenor_matrix& m = mats[i];
+                if (m.M != M || (m.dtype == TSENOR_BF16 ? 1 : 0) != b) continue;
+                MatJob j = make_job(m.W, m.dtype, m.rows, m.cols, m.ld, m.N, m.M, m.mask_out,
+                                    m.frac_out);
+                j.group_begin = c.groups;
+                c.groups += groups_of(j);
+                st->jobs_host[filled++] = j;
+                ++c.n;
+            }
+            if (c.n == 0) continue;
+            c.grid = clamp_grid(c.groups, st->num_cu, st->occ_batched[b][M]);
+            max_grid = c.grid > max_grid ? c.grid : max_grid;
+            cls[ncls++] = c;
+        }
+    if ((st_code = ensure_scratch(*st, (size_t)max_grid)) != TSENOR_OK) return st_code;
     Params prm;
     prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
     prm.iters = iters;
@@ -263,8 +278,17 @@ int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int ite
     e = hipMemcpyAsync(st->jobs_dev, st->jobs_host, sizeof(MatJob) * (size_t)count,
                        hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
-    e = (hipError_t)tsenor::launch_batched(st->jobs_dev, count, total, 32, prm, (int)grid, stream);
-    if (e != hipSuccess) return hip_fail(e, "batched kernel launch");
+    // The launches run in stream order, so they share the workspace.
+    for (int k = 0; k < ncls; ++k) {
+        const Class& c = cls[k];
+        e = (hipError_t)tsenor::launch_batched(st->jobs_dev + c.first, c.n, c.groups, c.M, c.bf16,
+                                               prm, (int)c.grid, stream);
+        if (e != hipSuccess) {
+            // earlier classes may be in flight: keep the workspace ordering
+            (void)record_end(*st, s);
+            return hip_fail(e, "batched kernel launch");
+        }
+    }
     return record_end(*st, s);
 }
 

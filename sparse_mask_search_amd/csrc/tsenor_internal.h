@@ -11,7 +11,7 @@ struct MatJob {
     uint32_t* mask;     // device, [rows][wpr]
     float* frac;        // device, [rows][cols] or nullptr
     int64_t rows, cols, ld, wpr;
-    int64_t group_begin;  // first global group id of this matrix (batched launch)
+    int64_t group_begin;  // batched launch: first group id of this matrix within its (M, dtype) class
     int32_t N, M;
     int32_t bf16;       // 1 = bfloat16 weights, 0 = fp32
     int32_t aligned;    // 1 = W rows may be read with 16-byte vector loads
@@ -38,11 +38,11 @@ int blocks_per_group(int M);
 int launch_mask(const MatJob& job, const Params& prm, int grid, void* stream);
 int launch_round(const MatJob& job, const float* S, int64_t lds, int ls_steps, int grid,
                  void* stream);
-int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int max_m,
+int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int M, int bf16,
                    const Params& prm, int grid, void* stream);
 // Number of 64-lane workgroups of each kernel that fit on one CU at once.
 int occupancy_mask(int M, int bf16);
 int occupancy_round(int M, int bf16);
-int occupancy_batched();
+int occupancy_batched(int M, int bf16);
 
 }  // namespace tsenor

@@ -78,11 +78,14 @@ template <int M> constexpr int dyk_lds_floats() {
 // share a 32-lane half hit distinct banks.
 template <int M> constexpr int kStageRow = M + 4;
 template <int M> constexpr int kStageBlk = M * (M + 4) + (M < 32 ? M : 0);
-template <int M> constexpr int rnd_lds_floats() { return (kWave / M) * kStageBlk<M> + kWave; }
+// |W| for the local search follows the staging area: block q, row i at
+// (q*M + i)*(M+1); then one word per lane for the rows of the current mask.
+template <int M> constexpr int rnd_lds_floats() {
+    return (kWave / M) * kStageBlk<M> + (kWave / M) * M * (M + 1) + kWave;
+}
 template <int M> constexpr int lds_floats() {
     return dyk_lds_floats<M>() > rnd_lds_floats<M>() ? dyk_lds_floats<M>() : rnd_lds_floats<M>();
 }
-constexpr int kMaxLdsFloats = lds_floats<32>() > lds_floats<16>() ? lds_floats<32>() : lds_floats<16>();
 
 template <int M> constexpr uint32_t kFull = (M == 32) ? 0xFFFFFFFFu : ((1u << M) - 1u);
 
@@ -192,11 +195,11 @@ __device__ __forceinline__ float row_allreduce(float x) {
 // stores them to the block's broadcast row, from which every lane reads its
 // own CW columns.  KIND 0 broadcasts the totals (combine = max or sum);
 // KIND 1 turns each total C_j into V_j * N / C_j with V_j the value currently
-// in the broadcast row, and returns whether any new V_j of this lane left
-// [2^-40, 2^40].
+// in the broadcast row and, when `check` is set, returns whether any new V_j
+// of this lane left [2^-40, 2^40].
 template <int M, int KIND, bool MAXOP>
 __device__ __forceinline__ bool col_exchange(const float (&part)[kCW<M>], float (&out)[kCW<M>],
-                                             float* lds, int blk, int lb, float fN) {
+                                             float* lds, int blk, int lb, float fN, bool check) {
     constexpr int CW = kCW<M>, G = kG<M>, H = kH<M>, CPL = kCPL<M>;
     const int g = lb / H, h = lb % H;
     float* mine = lds + blk * kBlkStride<M> + g * kRowStride<M> + h * CW;
@@ -219,14 +222,12 @@ __device__ __forceinline__ bool col_exchange(const float (&part)[kCW<M>], float 
     float* bc = lds + kBcastOff<M> + blk * kRowStride<M>;
     bool bad = false;
     if constexpr (KIND == 1) {
-        float lo = 0x1p40f, hi = 0x1p-40f;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            acc[c] = bc[lb * CPL + c] * (fN * rcpf(acc[c]));
-            lo = fminf(lo, acc[c]);
-            hi = fmaxf(hi, acc[c]);
+        for (int c = 0; c < CPL; ++c) acc[c] = bc[lb * CPL + c] * (fN * rcpf(acc[c]));
+        if (check) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) bad |= !(acc[c] >= 0x1p-40f && acc[c] <= 0x1p40f);
         }
-        bad = !(lo >= 0x1p-40f && hi <= 0x1p40f);
     }
 #pragma unroll
     for (int c = 0; c < CPL; ++c) bc[lb * CPL + c] = acc[c];
@@ -321,7 +322,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 #pragma unroll
             for (int c = 0; c < CW; ++c) cmax[c] = part[c];
         } else {
-            col_exchange<M, 0, true>(part, cmax, lds, blk, lb, fN);
+            col_exchange<M, 0, true>(part, cmax, lds, blk, lb, fN, false);
         }
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
@@ -334,7 +335,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 #pragma unroll
             for (int c = 0; c < CW; ++c) csum[c] = part[c];
         } else {
-            col_exchange<M, 0, false>(part, csum, lds, blk, lb, fN);
+            col_exchange<M, 0, false>(part, csum, lds, blk, lb, fN, false);
         }
         // C3 of cycle 1 is carried by P = 2^Y: X = min(Y, 0) appears as min(P V U, 1)
 #pragma unroll
@@ -394,7 +395,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                 bad = !(lo >= 0x1p-40f && hi <= 0x1p40f);
             }
         } else {
-            bad = col_exchange<M, 1, false>(cacc, V, lds, blk, lb, fN);
+            bad = col_exchange<M, 1, false>(cacc, V, lds, blk, lb, fN, (it & 3) == 0);
         }
         if ((it & 3) != 0) continue;
 #pragma unroll
@@ -586,26 +587,27 @@ __device__ __forceinline__ uint32_t float_to_ord(float f) {
 __device__ __forceinline__ float ord_to_float(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int s) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, s);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), s);
-    return ((uint64_t)hi << 32) | lo;
-}
-template <int M>
-__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) {
-#pragma unroll
-    for (int s = 1; s < M; s <<= 1) {
-        const uint64_t o = shfl_xor_u64(v, s);
-        v = o > v ? o : v;
+// Maximum / sum over each aligned group of M lanes, one DPP or permlane move
+// per step (no LDS round trip).  All 64 lanes must be active.
+template <int S, int M>
+__device__ __forceinline__ uint64_t max_u64_step(uint64_t v) {
+    if constexpr (S >= M) {
+        return v;
+    } else {
+        const uint32_t lo = xor_lane<S>((uint32_t)v), hi = xor_lane<S>((uint32_t)(v >> 32));
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        return max_u64_step<2 * S, M>(o > v ? o : v);
     }
-    return v;
 }
 template <int M>
-__device__ __forceinline__ int group_sum(int v) {
-#pragma unroll
-    for (int s = 1; s < M; s <<= 1) v += __shfl_xor(v, s);
-    return v;
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t v) { return max_u64_step<1, M>(v); }
+template <int S, int M>
+__device__ __forceinline__ int sum_step(int v) {
+    if constexpr (S >= M) return v;
+    else return sum_step<2 * S, M>(v + (int)xor_lane<S>((uint32_t)v));
 }
+template <int M>
+__device__ __forceinline__ int group_sum(int v) { return sum_step<1, M>(v); }
 
 // Greedy over the (S desc, index asc) order, as the fixed point of the row
 // and column thresholds; returns row i of the accepted mask.
@@ -663,19 +665,29 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     const int q = lane / M, i = lane % M;
     const int N = job.N;
 
-    // Stage the pass's blocks in LDS (row stride M+1: column reads are
-    // conflict-free), then sort row i and column i by key and keep only the
-    // bit of each sorted entry.
-    float* Ss = lds;  // [G] blocks of [M][M+4]
+    // Stage the pass's blocks in LDS, then sort row i and column i by key and
+    // keep only the bit of each sorted entry.  Row i of |W| is fetched in the
+    // same round trip as row i of S: most blocks need it for the local search.
+    float* Ss = lds;                                                     // [G][M][M+4]
+    float* As = lds + G * kStageBlk<M>;                                  // [G][M][M+1]
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(As + G * M * (M + 1));  // [G][M]
     {
-        float v[M];
+        float v[M], a[M];
         load_row_f32<M>(Sb + i * sld, (reinterpret_cast<uintptr_t>(Sb) & 15u) == 0 && (sld & 3) == 0, v);
+        if (valid) {
+            load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, a);
+        } else {
+#pragma unroll
+            for (int j = 0; j < M; ++j) { v[j] = 0.f; a[j] = 0.f; }
+        }
         float* dst = Ss + q * kStageBlk<M> + i * kStageRow<M>;
 #pragma unroll
         for (int k4 = 0; k4 < M / 4; ++k4)
             *reinterpret_cast<float4*>(dst + 4 * k4) =
-                valid ? make_float4(v[4 * k4], v[4 * k4 + 1], v[4 * k4 + 2], v[4 * k4 + 3])
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+                make_float4(v[4 * k4], v[4 * k4 + 1], v[4 * k4 + 2], v[4 * k4 + 3]);
+        float* Ai = As + (q * M + i) * (M + 1);
+#pragma unroll
+        for (int j = 0; j < M; ++j) Ai[j] = a[j];
     }
     __syncthreads();
     uint32_t rpb[M], cpb[M];
@@ -705,7 +717,6 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();  // Ss is reused below
 
     // ---- greedy as the fixed point of the row / column thresholds ----
     const uint32_t ulane = (uint32_t)lane;
@@ -722,18 +733,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     // ---- local search (R2) and fill (R3) ----
     const bool need = valid && D > 0;
     if (__ballot(need) != 0ull) {
-        float* As = lds;                                                   // [G][M][M+1]
-        uint32_t* Zs = reinterpret_cast<uint32_t*>(lds + G * M * (M + 1));  // [G][M]
-        float arow[M];
-        if (need) {  // only blocks with a shortfall read their |W| again
-            load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, arow);
-        } else {
-#pragma unroll
-            for (int j = 0; j < M; ++j) arow[j] = 0.f;
-        }
-        float* Ai = As + (q * M + i) * (M + 1);
-#pragma unroll
-        for (int j = 0; j < M; ++j) Ai[j] = arow[j];
+        const float* Ai = As + (q * M + i) * (M + 1);
         Zs[q * M + i] = Z;
         __syncthreads();
 
@@ -829,8 +829,9 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     // ---- pack: OR the blocks of one 32-column word together, one store ----
     const int bit0 = (int)((bc * M) & 31);
     uint32_t w = valid ? (Z << bit0) : 0u;
-#pragma unroll
-    for (int s = M; s < 32; s <<= 1) w |= (uint32_t)__shfl_xor((int)w, s);
+    if constexpr (M <= 4) w |= xor_lane<4>(w);
+    if constexpr (M <= 8) w |= xor_lane<8>(w);
+    if constexpr (M <= 16) w |= xor_lane<16>(w);
     if (valid && bit0 == 0) job.mask[(br * M + i) * job.wpr + ((bc * M) >> 5)] = w;
 }
 
@@ -882,9 +883,14 @@ __global__ __launch_bounds__(kWave) void round_kernel(MatJob job, const float* _
     }
 }
 
+// Many matrices of one (M, dtype) class in one launch: `jobs` lists the
+// class's matrices with group_begin = prefix sum of their group counts; the
+// grid walks the concatenated group range.  One kernel per class keeps the
+// register allocation of each path as tight as in mask_kernel.
+template <int M, bool BF16>
 __global__ __launch_bounds__(kWave) void batched_kernel(const MatJob* __restrict__ jobs, int count,
                                                         int64_t total_groups, Params prm) {
-    __shared__ __attribute__((aligned(16))) float lds[kMaxLdsFloats];
+    __shared__ __attribute__((aligned(16))) float lds[lds_floats<M>()];
     float* slot = prm.scratch + (int64_t)blockIdx.x * kSlotFloats;
     for (int64_t g = blockIdx.x; g < total_groups; g += gridDim.x) {
         int lo = 0, hi = count - 1;
@@ -893,18 +899,7 @@ __global__ __launch_bounds__(kWave) void batched_kernel(const MatJob* __restrict
             if (jobs[mid].group_begin <= g) lo = mid; else hi = mid - 1;
         }
         const MatJob job = jobs[lo];
-        const int64_t gl = g - job.group_begin;
-        switch (job.M * 2 + job.bf16) {
-            case 8: process_group<4, false>(job, prm, gl, slot, lds); break;
-            case 9: process_group<4, true>(job, prm, gl, slot, lds); break;
-            case 16: process_group<8, false>(job, prm, gl, slot, lds); break;
-            case 17: process_group<8, true>(job, prm, gl, slot, lds); break;
-            case 32: process_group<16, false>(job, prm, gl, slot, lds); break;
-            case 33: process_group<16, true>(job, prm, gl, slot, lds); break;
-            case 64: process_group<32, false>(job, prm, gl, slot, lds); break;
-            case 65: process_group<32, true>(job, prm, gl, slot, lds); break;
-            default: break;
-        }
+        process_group<M, BF16>(job, prm, g - job.group_begin, slot, lds);
     }
 }
 
@@ -954,10 +949,11 @@ int launch_round(const MatJob& job, const float* S, int64_t lds, int ls_steps, i
     return (int)hipGetLastError();
 }
 
-int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int /*max_m*/,
+int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int M, int bf16,
                    const Params& prm, int grid, void* stream) {
-    hipLaunchKernelGGL(batched_kernel, dim3(grid), dim3(kWave), 0, (hipStream_t)stream, jobs_dev,
-                       count, total_groups, prm);
+    TSENOR_DISPATCH(M, bf16,
+                    hipLaunchKernelGGL((batched_kernel<MM, B>), dim3(grid), dim3(kWave), 0,
+                                       (hipStream_t)stream, jobs_dev, count, total_groups, prm));
     return (int)hipGetLastError();
 }
 
@@ -977,9 +973,11 @@ int occupancy_round(int M, int bf16) {
     return n;
 }
 
-int occupancy_batched() {
+int occupancy_batched(int M, int bf16) {
     int n = 0;
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, batched_kernel, kWave, 0);
+    TSENOR_DISPATCH(M, bf16,
+                    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, batched_kernel<MM, B>,
+                                                                       kWave, 0));
     return n;
 }
 

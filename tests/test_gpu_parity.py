@@ -220,3 +220,60 @@ def test_model7b_layer_batched():
         ids = sample_block_ids((rows // M) * (cols // M), 60, 3)
         S64, _ = oracle.dykstra_blocks(Wf, N, M, wl.MODEL7B_TAU, wl.MODEL7B_ITERS, ids)
         assert np.abs(gather_blocks(f.cpu().numpy(), M, ids, cols) - S64).max() < S_TOL, nm
+
+
+def test_batched_mixed_classes():
+    """A batch that interleaves every (M, dtype) class, with ragged shapes and
+    a strided matrix, equals per-matrix calls and the oracle's rounding of the
+    GPU's own S, block for block."""
+    import torch
+    rng = np.random.default_rng(77)
+    specs = [(32, 16, 64, 96, "bf16"), (4, 2, 8, 36, "f32"), (16, 5, 48, 80, "bf16"),
+             (8, 3, 24, 40, "f32"), (32, 31, 32, 64, "f32"), (4, 1, 12, 20, "bf16"),
+             (8, 8, 16, 16, "bf16"), (16, 8, 32, 48, "f32")]
+    _note("batched mixed classes")
+    items, Ws, bits = [], [], []
+    for M, N, rows, cols, dt in specs:
+        W = rng.standard_normal((rows, cols)).astype(np.float32)
+        Wn = wl.f32_to_bf16_bits(W) if dt == "bf16" else W
+        Wt = to_device(Wn)
+        if M == 16 and dt == "f32":  # strided rows: ld = cols + 8
+            big = torch.zeros((rows, cols + 8), dtype=torch.float32, device="cuda")
+            big[:, :cols] = Wt
+            Wt = big[:, :cols]
+        items.append((Wt, N, M))
+        Ws.append(Wt)
+        bits.append(Wn)
+    tau, iters, ls = 25.0, 40, 6
+    outs = sms.mask_batched(items, tau, iters, ls, return_frac=True)
+    torch.cuda.synchronize()
+    for (Wt, N, M), Wn, (m, f) in zip(items, bits, outs):
+        m1, f1 = sms.mask(Wt, N, M, tau, iters, ls, return_frac=True)
+        torch.cuda.synchronize()
+        assert torch.equal(m, m1) and torch.equal(f, f1), (N, M)
+        rows, cols = Wt.shape
+        assert_feasible(words(m), rows, cols, N, M)
+        Wf = as_f32(Wn)
+        ref, _ = oracle.round_matrix(f.cpu().numpy(), Wf, N, M, ls)
+        assert np.array_equal(words(m), ref), (N, M)
+        S64, _ = oracle.dykstra_blocks(Wf, N, M, tau, iters,
+                                       np.arange((rows // M) * (cols // M)))
+        assert np.abs(gather_blocks(f.cpu().numpy(), M, np.arange(S64.shape[0]), cols)
+                      - S64).max() < S_TOL
+
+
+def test_output_buffers_are_checked():
+    """Caller-supplied mask / frac buffers of the wrong shape, dtype or layout
+    are refused before anything is enqueued."""
+    import torch
+    W = to_device(np.ones((32, 64), np.float32))
+    bad = [torch.empty((32, 1), dtype=torch.int32, device="cuda"),
+           torch.empty((32, 2), dtype=torch.int64, device="cuda"),
+           torch.empty((2, 32), dtype=torch.int32, device="cuda").t()]
+    for out in bad:
+        with pytest.raises(ValueError):
+            sms.mask(W, 2, 4, 10.0, 5, 1, out=out)
+    with pytest.raises(ValueError):
+        sms.mask(W, 2, 4, 10.0, 5, 1, frac_out=torch.empty((32, 32), device="cuda"))
+    with pytest.raises(ValueError):
+        sms.mask_batched([(W, 2, 4)], 10.0, 5, 1, outs=[])
