@@ -10,8 +10,8 @@
 // One 64-lane workgroup (one wave) owns a "group" of horizontally adjacent
 // blocks of one block-row and runs the whole path for them:
 //
-//  1. gather   each lane reads R full rows of its block straight from HBM
-//              (16-byte loads), |W| -> fp32, block max by lane shuffles.
+//  1. gather   each lane reads R rows of its tile straight from HBM
+//              (8/16-byte loads), |W| -> fp32, block max by lane shuffles.
 //  2. solve    first Dykstra cycle in log2 space (max-shifted log-sum-exp on
 //              rows and columns, robust for any tau); every later cycle in
 //              scaling form.  With Y = X + Q the cycle is Y += a_i + b_j and
@@ -20,11 +20,12 @@
 //                 E_ij = min(P_ij V_j U_i, 1)     (= exp(X_ij))          (C3)
 //                 a_i  = N / sum_j E_ij,           U_i *= a_i            (C1)
 //                 b_j  = N / sum_i E_ij a_i,       V_j *= b_j            (C2)
-//              i.e. 4 full-rate fp32 VALU ops per element -- mul, mul with
-//              the clamp output modifier (the clip; v_min is half rate on
-//              this chip), add, fma -- and no transcendental per element.  Rows live in lanes; column sums of blocks spread over
-//              several lanes are reduced through LDS (reduce-scatter, then a
-//              broadcast of the new V).
+//              i.e. 4 fp32 VALU ops per element -- mul, mul with the clamp
+//              output modifier (the clip), add, fma -- and no transcendental
+//              per element.  Rows live in lanes; the column sums of blocks
+//              spread over several lanes meet in a DPP butterfly
+//              (reduce-scatter, per-owner update of V, all-gather), so the
+//              solve touches no LDS.
 //  3. export   S = min(P V U, 1) is written to the workgroup's scratch slot
 //              (and to frac_out when asked).
 //  4. round    blocks are re-read from the slot one row and one column per
@@ -51,8 +52,8 @@ namespace {
 
 // Solve layout: each lane holds an R x CW tile (R rows, CW = M/H columns) of
 // one block, a block spans L = (M/R)*H lanes and a group is BPG = 64/L
-// blocks.  Row sums are completed across the H lanes of a row group by DPP,
-// column sums across the G = M/R row groups through LDS.
+// blocks.  Row sums are completed across the H lanes of a row group, column
+// sums across the G = M/R row groups, both by DPP moves.
 template <int M> struct Geo;
 template <> struct Geo<4> { static constexpr int R = 4, H = 1; };
 template <> struct Geo<8> { static constexpr int R = 8, H = 1; };
@@ -67,11 +68,38 @@ template <int M> constexpr int kBPG = kWave / kL<M>;     // blocks per group
 template <int M> constexpr int kCPL = M / kL<M>;         // columns finalised per lane
 static_assert(kBPG<32> * 32 % 32 == 0 && kBPG<16> * 16 % 32 == 0, "groups cover whole words");
 
+// Column sums of blocks spread over several lanes (M = 16 and 32) meet in
+// one of two ways, whichever measured faster for the tile shape:
+//  * M = 16 (4 lanes per block, one row group each): partial sums go through
+//    LDS -- reduce-scatter, then a broadcast of the new column scales.
+//  * M = 32 (8 lanes per block, 4 row groups x 2 row halves): a DPP
+//    butterfly in registers.  Every cross-lane step is then one DPP move
+//    inside an aligned group of 8 lanes: the two halves of a row pair up by
+//    one pattern, and the 4 row groups by two further patterns g1, g0 that
+//    commute with it.  Block lane lb = bits (b2 b1 b0): g1 = b2, g0 = b0^b2,
+//    h = b1^b2; row halves pair as lane^2 (quad_perm [2,3,0,1]), g1 as
+//    lane^7 (row_half_mirror), g0 as lane^1.  Row group g = 2*g1 + g0 holds
+//    rows g*R .. g*R+R-1, and its CW = 16 columns are stored with the
+//    4-column quads permuted: register quad k holds column quad k ^ g.  Two
+//    lanes that differ only in g1 then hold each other's register quads 0-1
+//    in their quads 2-3, and lanes that differ only in g0 hold each other's
+//    quad 0 in quad 1, so the reduce-scatter of the column sums and the
+//    all-gather of the new scales are uniform DPP operations.
+template <int M> constexpr bool kBfly = (M == 32);
+struct Lanes32 {
+    static constexpr int kRow = 0x4E, kG1 = 0x141, kG0 = 0xB1;
+    __device__ static int g(int lb) { return 2 * (lb >> 2) + ((lb ^ (lb >> 2)) & 1); }
+    __device__ static int h(int lb) { return ((lb >> 1) ^ (lb >> 2)) & 1; }
+};
+static_assert(kCW<32> == 16 && kG<32> == 4 && kH<32> == 2, "the butterfly's tile shape");
+
+// LDS exchange (M = 16): partial rows of the G row groups per block, then the
+// broadcast rows of V.
 template <int M> constexpr int kRowStride = M + 4;                      // floats per partial row
 template <int M> constexpr int kBlkStride = kG<M> * kRowStride<M>;      // floats per block
 template <int M> constexpr int kBcastOff = kBPG<M> * kBlkStride<M>;     // start of V rows
 template <int M> constexpr int dyk_lds_floats() {
-    return kL<M> == 1 ? 0 : kBcastOff<M> + kBPG<M> * kRowStride<M>;
+    return (kL<M> == 1 || kBfly<M>) ? 0 : kBcastOff<M> + kBPG<M> * kRowStride<M>;
 }
 // Rounding staging: block q of a pass at q*kStageBlk, row i at i*(M+4); the
 // block stride is M (mod 32) apart so that column reads of the blocks that
@@ -146,6 +174,26 @@ __device__ __forceinline__ void load_abs_row(const void* W, int64_t off, bool ve
     }
 }
 
+// In place: quad k of x becomes quad k ^ sw (sw in 0..3), by two conditional
+// swaps (the loads stay contiguous; the permutation is lane dependent).
+__device__ __forceinline__ void permute_quads(float (&x)[16], int sw) {
+    const bool s2 = (sw & 2) != 0, s1 = (sw & 1) != 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const float lo = x[c], hi = x[c + 8];
+        x[c] = s2 ? hi : lo;
+        x[c + 8] = s2 ? lo : hi;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; k += 8)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float lo = x[k + c], hi = x[k + c + 4];
+            x[k + c] = s1 ? hi : lo;
+            x[k + c + 4] = s1 ? lo : hi;
+        }
+}
+
 // M consecutive fp32 values (16-byte loads when `vec`).
 template <int M>
 __device__ __forceinline__ void load_row_f32(const float* p, bool vec, float (&out)[M]) {
@@ -174,19 +222,45 @@ __device__ __forceinline__ float tree_sum(const float (&v)[M]) {
     return s[0];
 }
 
-// Sum / max of x over the H lanes of a row group (adjacent lanes), by DPP.
-template <int H, bool MAXOP>
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum / max of x over the H lanes that share a tile row (all lanes active).
+template <int M, bool MAXOP>
 __device__ __forceinline__ float row_allreduce(float x) {
-    if constexpr (H >= 2) {
-        const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-        x = MAXOP ? fmaxf(x, y) : x + y;  // quad_perm [1,0,3,2]: lane ^ 1 (all lanes active)
+    if constexpr (kH<M> == 2) {
+        static_assert(kBfly<M>, "row halves pair by the butterfly layout");
+        const float y = dpp_mov<Lanes32::kRow>(x);
+        x = MAXOP ? fmaxf(x, y) : x + y;
     }
-    if constexpr (H >= 4) {
-        const float y = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
-        x = MAXOP ? fmaxf(x, y) : x + y;  // quad_perm [2,3,0,1]: lane ^ 2
-    }
-    static_assert(H == 1 || H == 2 || H == 4, "H");
+    static_assert(kH<M> == 1 || kH<M> == 2, "H");
     return x;
+}
+
+// Butterfly (M = 32): on return x[0..3] of every lane hold the column totals
+// (max or sum over the 4 row groups) of those register columns; each column
+// is owned by exactly one lane of the block per row half.
+template <bool MAXOP>
+__device__ __forceinline__ void col_reduce_scatter(float (&x)[16]) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const float y = dpp_mov<Lanes32::kG1>(x[c + 8]);
+        x[c] = MAXOP ? fmaxf(x[c], y) : x[c] + y;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float y = dpp_mov<Lanes32::kG0>(x[c + 4]);
+        x[c] = MAXOP ? fmaxf(x[c], y) : x[c] + y;
+    }
+}
+// Inverse: from the owners' x[0..3], every lane gets x[0..15] for its columns.
+__device__ __forceinline__ void col_all_gather(float (&x)[16]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c + 4] = dpp_mov<Lanes32::kG0>(x[c]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c + 8] = dpp_mov<Lanes32::kG1>(x[c]);
 }
 
 // Column totals of a block whose rows are spread over G row groups: lane
@@ -261,7 +335,9 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     constexpr int R = kR<M>, H = kH<M>, CW = kCW<M>, L = kL<M>;
     const int lane = threadIdx.x;
     const int blk = lane / L, lb = lane % L;
-    const int g = lb / H, h = lb % H;
+    int g = lb / H, h = lb % H;
+    if constexpr (kBfly<M>) { g = Lanes32::g(lb); h = Lanes32::h(lb); }
+    const int sw = kBfly<M> ? g : 0;  // register quad k holds column quad k ^ sw
     const int64_t nbc = job.cols / M;
     const int64_t bc = bc0 + blk;
     const bool valid = bc < nbc;
@@ -276,6 +352,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     for (int r = 0; r < R; ++r) {
         if (valid) {
             load_abs_row<CW, BF16>(job.W, (row0 + r) * job.ld + col0, vec, P[r]);
+            if constexpr (kBfly<M>) permute_quads(P[r], sw);
         } else {
 #pragma unroll
             for (int c = 0; c < CW; ++c) P[r][c] = 0.f;
@@ -301,11 +378,11 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         float mx = P[r][0];
 #pragma unroll
         for (int c = 1; c < CW; ++c) mx = fmaxf(mx, P[r][c]);
-        mx = row_allreduce<H, true>(mx);
+        mx = row_allreduce<M, true>(mx);
         float e[CW];
 #pragma unroll
         for (int c = 0; c < CW; ++c) e[c] = ex2(P[r][c] - mx);
-        const float a = log2N - mx - lg2(row_allreduce<H, false>(tree_sum<CW>(e)));
+        const float a = log2N - mx - lg2(row_allreduce<M, false>(tree_sum<CW>(e)));
 #pragma unroll
         for (int c = 0; c < CW; ++c) P[r][c] += a;
     }
@@ -318,11 +395,16 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             for (int r = 1; r < R; ++r) v = fmaxf(v, P[r][c]);
             part[c] = v;
         }
-        if constexpr (L == 1) {
+        if constexpr (kBfly<M>) {
 #pragma unroll
             for (int c = 0; c < CW; ++c) cmax[c] = part[c];
-        } else {
+            col_reduce_scatter<true>(cmax);
+            col_all_gather(cmax);
+        } else if constexpr (L > 1) {
             col_exchange<M, 0, true>(part, cmax, lds, blk, lb, fN, false);
+        } else {
+#pragma unroll
+            for (int c = 0; c < CW; ++c) cmax[c] = part[c];
         }
 #pragma unroll
         for (int c = 0; c < CW; ++c) {
@@ -331,11 +413,16 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             for (int r = 0; r < R; ++r) v += ex2(P[r][c] - cmax[c]);
             part[c] = v;
         }
-        if constexpr (L == 1) {
+        if constexpr (kBfly<M>) {
 #pragma unroll
             for (int c = 0; c < CW; ++c) csum[c] = part[c];
-        } else {
+            col_reduce_scatter<false>(csum);
+            col_all_gather(csum);
+        } else if constexpr (L > 1) {
             col_exchange<M, 0, false>(part, csum, lds, blk, lb, fN, false);
+        } else {
+#pragma unroll
+            for (int c = 0; c < CW; ++c) csum[c] = part[c];
         }
         // C3 of cycle 1 is carried by P = 2^Y: X = min(Y, 0) appears as min(P V U, 1)
 #pragma unroll
@@ -352,7 +439,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     for (int c = 0; c < CW; ++c) V[c] = 1.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) U[r] = 1.f;
-    if constexpr (L > 1) {
+    if constexpr (!kBfly<M> && L > 1) {
         float* bcr = lds + kBcastOff<M> + blk * kRowStride<M>;
 #pragma unroll
         for (int c = 0; c < kCPL<M>; ++c) bcr[lb * kCPL<M> + c] = 1.f;
@@ -369,7 +456,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                 e[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
                 acc[c & 3] = (c < 4) ? e[c] : acc[c & 3] + e[c];
             }
-            const float rs = row_allreduce<H, false>((acc[0] + acc[1]) + (acc[2] + acc[3]));
+            const float rs = row_allreduce<M, false>((acc[0] + acc[1]) + (acc[2] + acc[3]));
             const float a = fN * rcpf(rs);
             U[r] *= a;
 #pragma unroll
@@ -394,6 +481,17 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                 for (int c = 1; c < CW; ++c) { lo = fminf(lo, V[c]); hi = fmaxf(hi, V[c]); }
                 bad = !(lo >= 0x1p-40f && hi <= 0x1p40f);
             }
+        } else if constexpr (kBfly<M>) {
+            // column totals by butterfly; each owner rescales its 4 columns
+            // and the new scales are gathered back
+            col_reduce_scatter<false>(cacc);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) V[c] = V[c] * (fN * rcpf(cacc[c]));
+            if ((it & 3) == 0) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bad |= !(V[c] >= 0x1p-40f && V[c] <= 0x1p40f);
+            }
+            col_all_gather(V);
         } else {
             bad = col_exchange<M, 1, false>(cacc, V, lds, blk, lb, fN, (it & 3) == 0);
         }
@@ -417,7 +515,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 #pragma unroll
                 for (int r = 0; r < R; ++r) U[r] = 1.f;
             }
-            if constexpr (L > 1) {
+            if constexpr (!kBfly<M> && L > 1) {
                 float* bcr = lds + kBcastOff<M> + blk * kRowStride<M>;
                 __syncthreads();
                 if (f) {
@@ -439,18 +537,18 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         float* srow = slot + blk * M * M + (g * R + r) * M + h * CW;
 #pragma unroll
         for (int q = 0; q < CW / 4; ++q)
-            *reinterpret_cast<float4*>(srow + 4 * q) =
+            *reinterpret_cast<float4*>(srow + 4 * (q ^ sw)) =
                 make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
         if (job.frac != nullptr && valid) {
             float* frow = job.frac + (row0 + r) * job.cols + col0;
             if (fvec) {
 #pragma unroll
                 for (int q = 0; q < CW / 4; ++q)
-                    *reinterpret_cast<float4*>(frow + 4 * q) =
+                    *reinterpret_cast<float4*>(frow + 4 * (q ^ sw)) =
                         make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
             } else {
 #pragma unroll
-                for (int c = 0; c < CW; ++c) frow[c] = s[c];
+                for (int c = 0; c < CW; ++c) frow[(c & 3) + 4 * ((c >> 2) ^ sw)] = s[c];
             }
         }
     }
