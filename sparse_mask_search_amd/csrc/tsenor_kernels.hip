@@ -555,20 +555,21 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 }
 
 // ---------------------------------------------------------------- round
-// Total order key of entry idx (= i*M + j) with fractional value s: a positive
-// normal double whose high bits are double(s) with the exponent raised by one
-// (so s = 0 stays normal) and whose free low mantissa bits hold MM-1-idx.
-// Larger key = earlier in (s descending, idx ascending).
+// Sort key of the entry at position `pos` of a row (pos = column j) or of a
+// column (pos = row r) with fractional value s.  High word: the fp32 bits of
+// s plus one in the double's exponent field, so for s >= 0 the key is a
+// positive normal double ordered like s; low word: M-1-pos.  In a row, idx =
+// i*M + j ascends with j, and in a column idx = r*M + i ascends with r, so a
+// larger key comes earlier in the (s descending, idx ascending) order.
 template <int M>
-__device__ __forceinline__ double make_key(float s, int idx) {
-    const double d = (double)(s + 0.0f);  // -0 -> +0
-    const uint64_t b = ((uint64_t)__double_as_longlong(d) + (1ull << 52)) |
-                       (uint64_t)(M * M - 1 - idx);
-    return __longlong_as_double((long long)b);
+__device__ __forceinline__ double make_key(float s, int pos, int zero) {
+    const uint32_t hi = __float_as_uint(s + 0.0f) + 0x00100000u;  // -0 -> +0
+    return __hiloint2double((int)hi, M - 1 - pos + zero);
 }
+// One-hot bit (1 << pos) of the entry a key was made from.
 template <int M>
-__device__ __forceinline__ int key_index(double key) {
-    return M * M - 1 - (int)((uint32_t)__double_as_longlong(key) & (uint32_t)(M * M - 1));
+__device__ __forceinline__ uint32_t key_bit(double key) {
+    return (1u << (M - 1)) >> ((uint32_t)__double2loint(key) & (uint32_t)(M - 1));
 }
 
 // Batcher's odd-even merge sort network (descending) on registers: 191
@@ -597,17 +598,19 @@ __device__ __forceinline__ void sort_desc(double (&a)[M]) {
 // k.  Returns the bits of the entries at positions up to and including the
 // N-th entry whose bit is set in `allowed` -- i.e. every entry whose key is
 // >= the N-th largest allowed key -- or all entries if fewer than N are
-// allowed (threshold "minus infinity").
+// allowed (threshold "minus infinity").  c = (allowed entries seen) - N is
+// negative exactly while the walk is inside the prefix, so its sign bit is
+// the inclusion mask: no compares, selects or condition registers.
 template <int M>
 __device__ __forceinline__ uint32_t walk(const uint32_t (&pb)[M], uint32_t allowed, int N) {
-    int cnt = 0;
+    int c = -N;
     uint32_t m = 0u;
 #pragma unroll
     for (int k = 0; k < M; ++k) {
-        m |= (cnt < N) ? pb[k] : 0u;
-        cnt += (allowed & pb[k]) != 0u ? 1 : 0;
+        m |= pb[k] & (uint32_t)(c >> 31);
+        c += __popc(allowed & pb[k]);
     }
-    return cnt < N ? kFull<M> : m;
+    return m | ((uint32_t)(c >> 31) & kFull<M>);
 }
 
 // Same walk for a compile-time N: the first N positions always lie inside
@@ -616,14 +619,14 @@ __device__ __forceinline__ uint32_t walk(const uint32_t (&pb)[M], uint32_t allow
 template <int M, int N>
 __device__ __forceinline__ uint32_t walk_tail(uint32_t head, const uint32_t (&tail)[M - N],
                                               uint32_t allowed) {
-    int cnt = __popc(allowed & head);
+    int c = __popc(allowed & head) - N;
     uint32_t m = head;
 #pragma unroll
     for (int k = 0; k < M - N; ++k) {
-        m |= (cnt < N) ? tail[k] : 0u;
-        cnt += (allowed & tail[k]) != 0u ? 1 : 0;
+        m |= tail[k] & (uint32_t)(c >> 31);
+        c += __popc(allowed & tail[k]);
     }
-    return cnt < N ? kFull<M> : m;
+    return m | ((uint32_t)(c >> 31) & kFull<M>);
 }
 
 __device__ __forceinline__ constexpr uint32_t lowmask(int s) {
@@ -789,15 +792,19 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     }
     __syncthreads();
     uint32_t rpb[M], cpb[M];
+    // An opaque zero in the keys' low words: with compile-time constants there
+    // the scheduler interleaves both sorts and runs out of registers.
+    int kzero = 0;
+    asm volatile("" : "+v"(kzero));
     {
         double key[M];
         const float* src = Ss + q * kStageBlk<M> + i * kStageRow<M>;
 #pragma unroll
-        for (int j = 0; j < M; ++j) key[j] = make_key<M>(src[j], i * M + j);
+        for (int j = 0; j < M; ++j) key[j] = make_key<M>(src[j], j, kzero);
         sort_desc<M>(key);
 #pragma unroll
         for (int k = 0; k < M; ++k) {
-            rpb[k] = 1u << (key_index<M>(key[k]) % M);
+            rpb[k] = key_bit<M>(key[k]);
             asm volatile("" : "+v"(rpb[k]));  // keep only the bit, not the index
         }
     }
@@ -806,11 +813,11 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
         double key[M];
         const float* src = Ss + q * kStageBlk<M> + i;
 #pragma unroll
-        for (int r = 0; r < M; ++r) key[r] = make_key<M>(src[r * kStageRow<M>], r * M + i);
+        for (int r = 0; r < M; ++r) key[r] = make_key<M>(src[r * kStageRow<M>], r, kzero);
         sort_desc<M>(key);
 #pragma unroll
         for (int k = 0; k < M; ++k) {
-            cpb[k] = 1u << (key_index<M>(key[k]) / M);
+            cpb[k] = key_bit<M>(key[k]);
             asm volatile("" : "+v"(cpb[k]));
         }
     }
