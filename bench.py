@@ -34,6 +34,27 @@ PEAK_VALU_TOPS = 256 * 128 * 2.4e9 / 1e12
 # per element and Dykstra cycle: P*V (mul), *U with clamp to [0,1] (the clip),
 # row sum (add), column sum (fma)
 OPS_PER_ELEM_ITER = 4
+KERNEL_SOURCE = os.path.join(ROOT, "sparse_mask_search_amd", "csrc", "tsenor_kernels.hip")
+# HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this benchmark
+# (profiles/mask_kernel_16x32_8192x28672_bf16.md), valid only for the kernel source
+# they were taken on.
+TRAFFIC = {
+    "16:32-8192x28672-bf16": {
+        "kernel_sha256": "d3f483bd7c5890f527ecba4b83c93b999824c28f1ca21db1d08c8543b6e31a86",
+        "read_bytes": 873682.875 * 1024 * 2.0, "write_bytes": 960197.84375 * 1024 * 1.0},
+}
+
+
+def measured_traffic(workload):
+    """Counter-based HBM bytes per launch, or None once the kernel has changed."""
+    import hashlib
+    t = TRAFFIC.get(workload)
+    if t is None:
+        return None
+    with open(KERNEL_SOURCE, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != t["kernel_sha256"]:
+            return None
+    return int(t["read_bytes"] + t["write_bytes"])
 
 
 def log(*a):
@@ -273,7 +294,7 @@ def main():
         "blocks_per_s": round(w.blocks / (ms_wall / 1e3), 1),
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_VALU_TOPS,
                      "unit": "Tops/s", "frac": round(achieved / PEAK_VALU_TOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(w.name),
                      "kernel": "mask_kernel (gather + Dykstra + rounding + pack, one launch)",
                      "kernel_ms": round(ms, 4),
                      "ops_per_launch": ops,
