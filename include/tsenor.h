@@ -72,7 +72,10 @@ typedef enum {
 } tsenor_status;
 
 /* Whole method (steps 1-3 above) on one matrix.
- *   W        device, [rows][ld] of dtype; read only.
+ *   W        device, [rows][ld] of dtype; read only.  Only |W| enters the
+ *            method, so any other importance measure can be optimised by
+ *            passing its (non-negative) score matrix here, e.g. |W_ij|*||X_j||
+ *            with activation norms ||X_j||; the mask then keeps the most score.
  *   N, M     pattern: N ones per row and column of every M x M block.
  *   tau      entropy strength (> = 0, finite), applied to block-max-normalised |W|.
  *   iters    Dykstra cycles (C1, C2, C3), >= 1; no convergence test.

@@ -92,6 +92,14 @@ struct Lanes32 {
     __device__ static int h(int lb) { return ((lb >> 1) ^ (lb >> 2)) & 1; }
 };
 static_assert(kCW<32> == 16 && kG<32> == 4 && kH<32> == 2, "the butterfly's tile shape");
+static_assert(kWave * kR<32> * kCW<32> <= kSlotFloats && kWave * kR<16> * kCW<16> <= kSlotFloats &&
+                  kWave * kR<8> * kCW<8> <= kSlotFloats && kWave * kR<4> * kCW<4> <= kSlotFloats,
+              "every lane's log2 kernel fits the workgroup's slot");
+// Blocks whose cycle-1 kernel reaches below 2^kDeepLog2 rescale in log2 space.
+// fp32 emulation of the iteration against the fp64 oracle: folding in the
+// linear domain stays within 5e-6 while the minimum is above ~-115 and fails
+// beyond the normal range (-126).
+constexpr float kDeepLog2 = -100.0f;
 
 // LDS exchange (M = 16): partial rows of the G row groups per block, then the
 // broadcast rows of V.
@@ -346,6 +354,9 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     const bool vec = job.aligned != 0;
     const int64_t row0 = br * M + g * R;      // first matrix row of this lane's tile
     const int64_t col0 = bc * M + h * CW;     // first matrix column of this lane's tile
+    // Lane's part of the slot (free until the export): the cycle-1 kernel Y in
+    // log2 units, kept only for "deep" blocks (see the rescaling below).
+    float* ylane = slot + lane * (R * CW);
 
     float P[R][CW];
 #pragma unroll
@@ -372,6 +383,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 #pragma unroll
         for (int c = 0; c < CW; ++c) P[r][c] *= scale;
 
+    bool deep;
     // ---- cycle 1 in log2 space (Q = 0, so no clip enters C1/C2) ----
 #pragma unroll
     for (int r = 0; r < R; ++r) {  // C1
@@ -425,11 +437,34 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             for (int c = 0; c < CW; ++c) csum[c] = part[c];
         }
         // C3 of cycle 1 is carried by P = 2^Y: X = min(Y, 0) appears as min(P V U, 1)
+        float b[CW];
 #pragma unroll
-        for (int c = 0; c < CW; ++c) {
-            const float b = log2N - cmax[c] - lg2(csum[c]);
+        for (int c = 0; c < CW; ++c) b[c] = log2N - cmax[c] - lg2(csum[c]);
+        float ymin = 0.f;
 #pragma unroll
-            for (int r = 0; r < R; ++r) P[r][c] = ex2(P[r][c] + b);
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int c = 0; c < CW; ++c) {
+                P[r][c] += b[c];
+                ymin = fminf(ymin, P[r][c]);
+            }
+        // A block is "deep" when its kernel spans more than fp32 can hold
+        // next to O(1) values (tau * log2(e) beyond ~100): its Y is kept so
+        // that rescaling happens in log2 space.
+        int dflag = (ymin < kDeepLog2) ? 1 : 0;
+#pragma unroll
+        for (int s = 1; s < L; s <<= 1) dflag |= __shfl_xor(dflag, s);
+        deep = dflag != 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (deep) {
+#pragma unroll
+                for (int q = 0; q < CW / 4; ++q)
+                    *reinterpret_cast<float4*>(ylane + r * CW + 4 * q) =
+                        make_float4(P[r][4 * q], P[r][4 * q + 1], P[r][4 * q + 2], P[r][4 * q + 3]);
+            }
+#pragma unroll
+            for (int c = 0; c < CW; ++c) P[r][c] = ex2(P[r][c]);
         }
     }
 
@@ -500,16 +535,43 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         for (int r = 0; r < R; ++r) bad |= !(U[r] >= 0x1p-40f && U[r] <= 0x1p40f);
         bad = bad && valid;
         if (__builtin_expect(__ballot(bad) != 0ull, 0)) {
-            // Rare: fold the scales into P (P <- P V U, scales <- 1) so that
-            // they stay far from the fp32 range limits.  Z = P U V is unchanged.
+            // Rare: fold the scales into the kernel (scales <- 1), so that
+            // P U V is unchanged but the scales stay far from the fp32 range
+            // limits.  Deep blocks fold in log2 space (Y <- Y + log2 U +
+            // log2 V, P <- 2^Y): folding into P itself would lose the entries
+            // of P that underflow, which can still grow to O(1) later.
             int f = bad ? 1 : 0;
 #pragma unroll
             for (int s = 1; s < L; s <<= 1) f |= __shfl_xor(f, s);
-            if (f) {
+            if (f && deep) {
+                float lv[CW];
+#pragma unroll
+                for (int c = 0; c < CW; ++c) lv[c] = lg2(V[c]);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float lu = lg2(U[r]);
+#pragma unroll
+                    for (int q = 0; q < CW / 4; ++q) {
+                        float4* yp = reinterpret_cast<float4*>(ylane + r * CW + 4 * q);
+                        float4 y = *yp;
+                        y.x += lu + lv[4 * q];
+                        y.y += lu + lv[4 * q + 1];
+                        y.z += lu + lv[4 * q + 2];
+                        y.w += lu + lv[4 * q + 3];
+                        *yp = y;
+                        P[r][4 * q] = ex2(y.x);
+                        P[r][4 * q + 1] = ex2(y.y);
+                        P[r][4 * q + 2] = ex2(y.z);
+                        P[r][4 * q + 3] = ex2(y.w);
+                    }
+                }
+            } else if (f) {
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int c = 0; c < CW; ++c) P[r][c] = (P[r][c] * V[c]) * U[r];
+            }
+            if (f) {
 #pragma unroll
                 for (int c = 0; c < CW; ++c) V[c] = 1.f;
 #pragma unroll

@@ -55,6 +55,12 @@ WORKLOADS = {
     "16:32-8192x28672-bf16": Workload(
         "16:32-8192x28672-bf16", 16, 32, 8192, 28672, "bf16", 40.0, 200, 32, 3,
         "0.015*student_t(3)*lognormal(0,0.5) per column"),
+    # The same matrix in the pages' default regime: temperature 0.005 * max|W|
+    # read as tau = 200 on block-max-normalised scores, 300 iterations, 10
+    # local-search steps.
+    "16:32-8192x28672-bf16-tau200": Workload(
+        "16:32-8192x28672-bf16-tau200", 16, 32, 8192, 28672, "bf16", 200.0, 300, 10, 3,
+        "0.015*student_t(3)*lognormal(0,0.5) per column (as 16:32-8192x28672-bf16)"),
 }
 
 # 7B-shaped model: per layer (seed 1000 + layer) q, k, v, o, gate, up, down.
@@ -119,6 +125,16 @@ def generate(name: str) -> np.ndarray:
             out[r0:r1] = f32_to_bf16_bits(x.astype(np.float32))
         return out
     raise KeyError(name)
+
+
+def wanda_scores(W: np.ndarray, seed: int) -> np.ndarray:
+    """Wanda-style importance scores |W_ij| * ||X_j|| as an fp32 matrix, with
+    synthetic per-input-column activation norms ||X_j|| ~ LogNormal(0, 1)
+    drawn from default_rng(seed) -- an example of a score matrix other than
+    |W| that the mask search can be run on."""
+    rng = np.random.default_rng(seed)
+    norms = rng.lognormal(0.0, 1.0, W.shape[1])
+    return (np.abs(W.astype(np.float64)) * norms[None, :]).astype(np.float32)
 
 
 def model7b_layer(layer: int, which=None):

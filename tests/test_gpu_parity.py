@@ -69,6 +69,28 @@ def test_small_parity(M, nbc, nbr, kind, bf16):
     assert_feasible(mask, rows, cols, N, M)
 
 
+@pytest.mark.parametrize("tau", [120.0, 300.0])
+@pytest.mark.parametrize("M,nbc,nbr", SMALL)
+def test_large_tau(M, nbc, nbr, tau):
+    """Kernels whose log2 range exceeds fp32's (tau * log2(e) well past 126):
+    the rescaling must then happen in log2 space or entries that underflow
+    are lost; S stays within the contract and masks exact."""
+    N = M // 2
+    iters, ls = 150, M
+    W_np = _small(300 + M, M, nbc, nbr, "outlier", M >= 16)
+    rows, cols = W_np.shape
+    _note(f"large tau={tau} M={M} {rows}x{cols}")
+    _, mask, S, mask2 = _run(W_np, N, M, tau, iters, ls)
+    Wf = as_f32(W_np)
+    S64, _ = oracle.dykstra(Wf, N, M, tau, iters)
+    err = np.abs(S - S64).max()
+    print(f"tau {tau} M {M}: max|S-S64| = {err:.3e}", flush=True)
+    assert err < S_TOL
+    ref, _ = oracle.round_matrix(S, Wf, N, M, ls)
+    assert np.array_equal(mask, ref) and np.array_equal(mask2, ref)
+    assert_feasible(mask, rows, cols, N, M)
+
+
 @pytest.mark.parametrize("M,N", [(4, 1), (8, 3), (16, 5), (32, 7), (32, 31), (16, 16)])
 def test_other_n(M, N):
     W_np = _small(7 + N, M, 11, 2, "student_t", True)
@@ -172,6 +194,7 @@ def test_workload_2_4_full():
     ("4:8-4096x4096-f32", 3000, 512),
     ("8:16-4096x11008-bf16", 1500, 256),
     ("16:32-8192x28672-bf16", 400, 128),
+    ("16:32-8192x28672-bf16-tau200", 300, 64),
 ])
 def test_workload_sampled(name, nsample, slab_rows):
     w, W_np, Wf = _workload(name)
@@ -277,3 +300,24 @@ def test_output_buffers_are_checked():
         sms.mask(W, 2, 4, 10.0, 5, 1, frac_out=torch.empty((32, 32), device="cuda"))
     with pytest.raises(ValueError):
         sms.mask_batched([(W, 2, 4)], 10.0, 5, 1, outs=[])
+
+
+@pytest.mark.parametrize("N,M,rows,cols", [(16, 32, 96, 192), (8, 16, 64, 160), (2, 4, 32, 48)])
+def test_generic_scores(N, M, rows, cols):
+    """Any non-negative score matrix can stand in for |W| (here Wanda-style
+    |W_ij| * ||X_j||): S and masks match the oracle run on the same scores, and
+    the local search scores moves with them."""
+    import torch
+    rng = np.random.default_rng(5 + M)
+    W = (0.02 * rng.standard_normal((rows, cols))).astype(np.float32)
+    Sc = wl.wanda_scores(W, 17 + M)
+    _note("generic scores", N, M)
+    Wt = to_device(Sc)
+    mask_t, S_t = sms.mask(Wt, N, M, 30.0, 120, 12, return_frac=True)
+    torch.cuda.synchronize()
+    S = S_t.cpu().numpy()
+    S64, _ = oracle.dykstra(Sc, N, M, 30.0, 120)
+    assert np.abs(S - S64).max() < S_TOL
+    ref, _ = oracle.round_matrix(S, Sc, N, M, 12)
+    assert np.array_equal(words(mask_t), ref)
+    assert_feasible(words(mask_t), rows, cols, N, M)
