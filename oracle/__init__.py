@@ -53,6 +53,9 @@ def _load():
                                               _P, _I64, _P, _P, _I]
         lib.oracle_round_block.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P]
         lib.oracle_round.argtypes = [_P, _I64, _P, _I64, _I64, _I64, _I, _I, _I, _P, _P, _I]
+        lib.oracle_round_block_ex.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
+        lib.oracle_round_ex.argtypes = [_P, _I64, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P, _P,
+                                        _P, _I]
         lib.oracle_exact_opt_block.argtypes = [_P, _I, _I, _P]
         lib.oracle_exact_opt_block.restype = _D
         lib.oracle_exact_opt_blocks.argtypes = [_P, _I64, _I64, _I64, _I, _I, _P, _I64, _P, _I]
@@ -139,6 +142,49 @@ def round_matrix(S32, W, N: int, M: int, ls_steps: int, nthreads: int = 0):
     stats = np.zeros(4, np.int64)
     _check(_load().oracle_round(_ptr(S32), cols, _ptr(W), cols, rows, cols, N, M, ls_steps,
                                 _ptr(mask), _ptr(stats), nthreads), "round")
+    return mask, stats
+
+
+def round_block_ex(S32, A, N: int, ls_steps: int, polish_steps: int, prev=None):
+    """round_block followed by the optional 2-opt polish (at most polish_steps
+    swaps) and the keep-better safeguard against `prev` (0/1 [M,M] or None).
+    Returns (Z, info, gains) with info = (shortfall, local-search moves, fill
+    moves, polish swaps, 1 if prev was kept) and the applied swap gains."""
+    S32 = np.ascontiguousarray(np.asarray(S32, dtype=np.float32))
+    A = np.ascontiguousarray(np.asarray(A, dtype=np.float32))
+    M = S32.shape[0]
+    Z = np.zeros((M, M), np.uint8)
+    info = np.zeros(5, np.int32)
+    gains = np.zeros(max(1, polish_steps), np.float32)
+    P = None if prev is None else np.ascontiguousarray(np.asarray(prev, dtype=np.uint8))
+    _check(_load().oracle_round_block_ex(_ptr(S32), _ptr(A), N, M, ls_steps, polish_steps,
+                                         _ptr(P) if P is not None else None, _ptr(Z),
+                                         _ptr(info), _ptr(gains)), "round_block_ex")
+    info = tuple(int(x) for x in info)
+    return Z, info, gains[:info[3]].copy()
+
+
+def round_matrix_ex(S32, W, N: int, M: int, ls_steps: int, polish_steps: int,
+                    prev_mask=None, nthreads: int = 0):
+    """round_matrix with the optional stages.  prev_mask: packed uint32 words
+    like the output, or None.  Returns (mask, stats) with stats = [blocks with
+    shortfall, total shortfall, R2 moves, R3 moves, R4 swaps, blocks that kept
+    the previous mask]."""
+    S32 = np.ascontiguousarray(np.asarray(S32, dtype=np.float32))
+    W = _f32(W)
+    rows, cols = W.shape
+    if S32.shape != W.shape:
+        raise ValueError("S32 and W shapes differ")
+    mask = np.zeros((rows, (cols + 31) // 32), np.uint32)
+    P = None
+    if prev_mask is not None:
+        P = np.ascontiguousarray(np.asarray(prev_mask, dtype=np.uint32))
+        if P.shape != mask.shape:
+            raise ValueError("prev_mask shape differs from the mask's")
+    stats = np.zeros(6, np.int64)
+    _check(_load().oracle_round_ex(_ptr(S32), cols, _ptr(W), cols, rows, cols, N, M, ls_steps,
+                                   polish_steps, _ptr(P) if P is not None else None, _ptr(mask),
+                                   _ptr(stats), nthreads), "round_ex")
     return mask, stats
 
 

@@ -239,6 +239,95 @@ static int round_block(const float* S, const float* A, int N, int M, int L,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Optional stages after R3 (the survey's "next" row f1; the pages describe no
+ * such step -- readings r4/r5 in the design notes):
+ *
+ * R4 2-opt polish, at most K swaps.  A swap takes kept (i, j) and (i', j'),
+ *    i < i', with Z_ij' = Z_i'j = 0, to (i, j') and (i', j); every row and
+ *    column keeps its count.  Its gain is evaluated in fp32 as
+ *    (A_ij' - A_i'j') + (A_i'j - A_ij), each difference rounded, then the sum.
+ *    The best gain is taken, ties to the smallest (i, j, i', j'); it is applied
+ *    only when > 0, else R4 ends.
+ * R5 keep-better safeguard against a caller's previous mask P: if P has N
+ *    ones in every row and column of the block and obj(P) > obj(Z), the block
+ *    takes P.  obj(Z) = sum over rows i ascending of (sum over j ascending of
+ *    A_ij Z_ij), both sums in fp64.                                          */
+static int polish_block(const float* A, int M, int K, uint8_t* Z, float* gains) {
+    int swaps = 0;
+    while (swaps < K) {
+        int found = 0, bi = 0, bj = 0, bip = 0, bjp = 0;
+        float best = 0.0f;
+        for (int i = 0; i < M; ++i)
+            for (int j = 0; j < M; ++j) {
+                if (!Z[i * M + j]) continue;
+                for (int ip = i + 1; ip < M; ++ip) {
+                    if (Z[ip * M + j]) continue;
+                    for (int jp = 0; jp < M; ++jp) {
+                        if (!Z[ip * M + jp] || Z[i * M + jp]) continue;
+                        volatile float t1 = A[i * M + jp] - A[ip * M + jp];
+                        volatile float t2 = A[ip * M + j] - A[i * M + j];
+                        float g = t1 + t2;
+                        if (!found || g > best) {
+                            found = 1;
+                            best = g;
+                            bi = i; bj = j; bip = ip; bjp = jp;
+                        }
+                    }
+                }
+            }
+        if (!found || !(best > 0.0f)) break;
+        if (gains) gains[swaps] = best;
+        Z[bi * M + bj] = 0;
+        Z[bi * M + bjp] = 1;
+        Z[bip * M + bjp] = 0;
+        Z[bip * M + bj] = 1;
+        ++swaps;
+    }
+    return swaps;
+}
+
+static double block_objective(const float* A, const uint8_t* Z, int M) {
+    double total = 0.0;
+    for (int i = 0; i < M; ++i) {
+        double row = 0.0;
+        for (int j = 0; j < M; ++j)
+            if (Z[i * M + j]) row += (double)A[i * M + j];
+        total += row;
+    }
+    return total;
+}
+
+static int block_feasible(const uint8_t* Z, int N, int M) {
+    for (int i = 0; i < M; ++i) {
+        int r = 0, c = 0;
+        for (int j = 0; j < M; ++j) {
+            r += Z[i * M + j] != 0;
+            c += Z[j * M + i] != 0;
+        }
+        if (r != N || c != N) return 0;
+    }
+    return 1;
+}
+
+/* R1-R3, then R4 and R5.  info[0..2] as in round_block, info[3] = R4 swaps,
+ * info[4] = 1 when the previous mask was taken.  prev may be NULL.          */
+static int round_block_ex(const float* S, const float* A, int N, int M, int L, int K,
+                          const uint8_t* prev, uint8_t* Z, int* order, int* info,
+                          float* gains) {
+    int st = round_block(S, A, N, M, L, Z, order, info, NULL, NULL);
+    info[3] = info[4] = 0;
+    if (st != OR_OK) return st;
+    info[3] = polish_block(A, M, K, Z, gains);
+    if (!block_feasible(Z, N, M)) return OR_ERR_INVARIANT;
+    if (prev && block_feasible(prev, N, M) &&
+        block_objective(A, prev, M) > block_objective(A, Z, M)) {
+        memcpy(Z, prev, (size_t)(M * M));
+        info[4] = 1;
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Exact optimum of one block ("Core claim": the LP over 0 <= S <= 1 with row
  * and column sums N is integral -- bipartite b-matching / capacitated OT).
  * Min-cost flow by successive shortest paths with Dijkstra on reduced costs:
@@ -465,6 +554,92 @@ int oracle_round(const float* S32, int64_t lds, const float* W, int64_t ld,
         stats[1] += s1;
         stats[2] += s2;
         stats[3] += s3;
+    }
+    return status;
+}
+
+/* oracle_round_block with the optional stages: polish_steps = K of R4 and
+ * prev (dense M*M 0/1, or NULL) for R5.  info[5] as in round_block_ex;
+ * gains (may be NULL) receives the applied R4 gains.                        */
+int oracle_round_block_ex(const float* S32, const float* A, int N, int M, int ls_steps,
+                          int polish_steps, const uint8_t* prev, uint8_t* Z, int* info,
+                          float* gains) {
+    if (M < 1 || M > 32 || N < 1 || N > M || ls_steps < 0 || polish_steps < 0) return OR_ERR_ARG;
+    int order[1024];
+    return round_block_ex(S32, A, N, M, ls_steps, polish_steps, prev, Z, order, info, gains);
+}
+
+/* oracle_round with the optional stages; prev_mask (packed like mask, or
+ * NULL) is the caller's previous mask.  stats (may be NULL) accumulates
+ * [blocks with D > 0, total D, R2 moves, R3 moves, R4 swaps, blocks that kept
+ * the previous mask].                                                       */
+int oracle_round_ex(const float* S32, int64_t lds, const float* W, int64_t ld,
+                    int64_t rows, int64_t cols, int N, int M, int ls_steps, int polish_steps,
+                    const uint32_t* prev_mask, uint32_t* mask, int64_t* stats, int nthreads) {
+    if (check_shape(rows, cols, ld, N, M) || lds < cols || ls_steps < 0 || polish_steps < 0)
+        return OR_ERR_ARG;
+    const int64_t nbc = cols / M, nb = (rows / M) * nbc, wpr = (cols + 31) / 32;
+    uint32_t* out = mask;
+    if (prev_mask == mask) { /* in place: keep the previous words readable */
+        out = (uint32_t*)malloc((size_t)(rows * wpr) * sizeof(uint32_t));
+        if (!out) return OR_ERR_ARG;
+    }
+    memset(out, 0, (size_t)(rows * wpr) * sizeof(uint32_t));
+    int status = OR_OK;
+    int64_t s0 = 0, s1 = 0, s2 = 0, s3 = 0, s4 = 0, s5 = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel reduction(+ : s0, s1, s2, s3, s4, s5)
+    {
+        float A[1024], S[1024];
+        uint8_t Z[1024], P[1024];
+        int order[1024], info[5];
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t id = 0; id < nb; ++id) {
+            int64_t bi = id / nbc, bj = id % nbc;
+            gather_abs(W, ld, bi, bj, M, A);
+            for (int i = 0; i < M; ++i)
+                for (int j = 0; j < M; ++j) {
+                    S[i * M + j] = S32[(bi * M + i) * lds + bj * M + j];
+                    if (prev_mask) {
+                        int64_t r = bi * M + i, c = bj * M + j;
+                        P[i * M + j] = (uint8_t)((prev_mask[r * wpr + c / 32] >> (c % 32)) & 1u);
+                    }
+                }
+            int st = round_block_ex(S, A, N, M, ls_steps, polish_steps, prev_mask ? P : NULL, Z,
+                                    order, info, NULL);
+            if (st != OR_OK) {
+#pragma omp atomic write
+                status = st;
+                continue;
+            }
+            s0 += info[0] > 0;
+            s1 += info[0];
+            s2 += info[1];
+            s3 += info[2];
+            s4 += info[3];
+            s5 += info[4];
+            for (int i = 0; i < M; ++i)
+                for (int j = 0; j < M; ++j)
+                    if (Z[i * M + j]) {
+                        int64_t r = bi * M + i, c = bj * M + j;
+#pragma omp atomic update
+                        out[r * wpr + c / 32] |= (uint32_t)1u << (c % 32);
+                    }
+        }
+    }
+    if (out != mask) {
+        memcpy(mask, out, (size_t)(rows * wpr) * sizeof(uint32_t));
+        free(out);
+    }
+    if (stats) {
+        stats[0] += s0;
+        stats[1] += s1;
+        stats[2] += s2;
+        stats[3] += s3;
+        stats[4] += s4;
+        stats[5] += s5;
     }
     return status;
 }
