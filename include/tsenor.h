@@ -87,6 +87,29 @@ int tsenor_mask(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld
                 float tau, int iters, int ls_steps, uint32_t* mask_out, float* frac_out,
                 void* stream);
 
+/* tsenor_mask followed by two optional stages per block (not on the pages; the
+ * survey of the method ranks them first among the next steps):
+ *   polish_steps  >= 0: at most this many 2-opt swaps after the fill.  A swap
+ *            takes kept (i, j) and (i', j'), i < i', with Z_ij' = Z_i'j = 0, to
+ *            (i, j') and (i', j), keeping every row and column count; its gain
+ *            is (|W_ij'| - |W_i'j'|) + (|W_i'j| - |W_ij|) in fp32 (each
+ *            difference rounded, then the sum).  The best gain is applied if
+ *            > 0, ties to the smallest (i, j, i', j'); 0 turns the stage off.
+ *   prev_mask device, same layout as mask_out, or NULL: a previous mask (e.g.
+ *            from an earlier pruning step).  A block takes the previous mask
+ *            when that has exactly N ones in every row and column and keeps
+ *            strictly more score, sum over rows i ascending of the row sums
+ *            over j ascending of |W_ij|, both in fp64; so the result is never
+ *            worse than the previous mask.  Blocks where the previous mask is
+ *            not feasible ignore it.  prev_mask may alias mask_out (in-place
+ *            update).
+ * Other arguments, errors and conventions as in tsenor_mask (polish_steps < 0
+ * is TSENOR_ERR_PARAM).  tsenor_mask(...) equals tsenor_mask_ex(..., 0, NULL, ...). */
+int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,
+                   float tau, int iters, int ls_steps, int polish_steps,
+                   const uint32_t* prev_mask, uint32_t* mask_out, float* frac_out,
+                   void* stream);
+
 /* One matrix of a batch.  Field meanings as in tsenor_mask.                    */
 typedef struct {
     const void* W;

@@ -46,6 +46,9 @@ def lib():
         l = ctypes.CDLL(_LIB_PATH)
         l.tsenor_mask.argtypes = [_P, _I, _I64, _I64, _I64, _I, _I, _F, _I, _I, _P, _P, _P]
         l.tsenor_mask.restype = _I
+        l.tsenor_mask_ex.argtypes = [_P, _I, _I64, _I64, _I64, _I, _I, _F, _I, _I, _I, _P, _P, _P,
+                                     _P]
+        l.tsenor_mask_ex.restype = _I
         l.tsenor_round.argtypes = [_P, _I64, _P, _I, _I64, _I64, _I64, _I, _I, _I, _P, _P]
         l.tsenor_round.restype = _I
         l.tsenor_mask_batched.argtypes = [ctypes.POINTER(_Matrix), _I, _F, _I, _I, _P]
@@ -104,12 +107,15 @@ def _mask_buffer(W, out=None):
 
 
 def mask(W, N: int, M: int, tau: float, iters: int, ls_steps: int, return_frac: bool = False,
-         out=None, frac_out=None, stream=None):
+         out=None, frac_out=None, stream=None, polish_steps: int = 0, prev_mask=None):
     """Transposable N:M mask of W (fp32 or bf16 CUDA tensor).
 
     Returns (mask, frac): mask is int32 [rows, ceil(cols/32)] holding the
     uint32 bit words (bit c%32 of word c/32 = column c); frac is the fp32
-    fractional solution S [rows, cols] if requested, else None."""
+    fractional solution S [rows, cols] if requested, else None.
+    polish_steps > 0 adds up to that many 2-opt swaps per block; prev_mask (a
+    mask tensor like the output, may be `out` itself) makes every block keep
+    it where it is feasible and keeps more |W| (tsenor_mask_ex)."""
     torch = _torch()
     dt = _weights(W)
     rows, cols = W.shape
@@ -121,12 +127,22 @@ def mask(W, N: int, M: int, tau: float, iters: int, ls_steps: int, return_frac: 
                                    or not frac_out.is_contiguous()):
         raise ValueError(f"frac_out must be a contiguous float32 tensor of shape {(rows, cols)} "
                          f"on {W.device}")
-    st = lib().tsenor_mask(ctypes.c_void_p(W.data_ptr()), dt, rows, cols, W.stride(0), N, M,
-                           float(tau), int(iters), int(ls_steps), ctypes.c_void_p(out.data_ptr()),
-                           ctypes.c_void_p(frac_out.data_ptr() if frac_out is not None else 0),
-                           _stream(stream))
+    fp = ctypes.c_void_p(frac_out.data_ptr() if frac_out is not None else 0)
+    if polish_steps == 0 and prev_mask is None:
+        st = lib().tsenor_mask(ctypes.c_void_p(W.data_ptr()), dt, rows, cols, W.stride(0), N, M,
+                               float(tau), int(iters), int(ls_steps),
+                               ctypes.c_void_p(out.data_ptr()), fp, _stream(stream))
+        if st != 0:
+            raise TsenorError(st, "tsenor_mask")
+        return out, frac_out
+    if prev_mask is not None:
+        prev_mask = _mask_buffer(W, prev_mask)  # same checks as an output buffer
+    st = lib().tsenor_mask_ex(ctypes.c_void_p(W.data_ptr()), dt, rows, cols, W.stride(0), N, M,
+                              float(tau), int(iters), int(ls_steps), int(polish_steps),
+                              ctypes.c_void_p(prev_mask.data_ptr() if prev_mask is not None else 0),
+                              ctypes.c_void_p(out.data_ptr()), fp, _stream(stream))
     if st != 0:
-        raise TsenorError(st, "tsenor_mask")
+        raise TsenorError(st, "tsenor_mask_ex")
     return out, frac_out
 
 

@@ -42,6 +42,9 @@ struct DeviceState {
     int occ_mask[2][33] = {};
     int occ_round[2][33] = {};
     int occ_batched[2][33] = {};
+    int occ_refine[2][33] = {};
+    uint32_t* prev_copy = nullptr;  // copy of a previous mask that aliases the output
+    size_t prev_cap = 0;            // words
 };
 DeviceState g_dev[kMaxDevices];
 
@@ -70,6 +73,7 @@ MatJob make_job(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld
     j.W = W;
     j.mask = mask;
     j.frac = frac;
+    j.prev = nullptr;
     j.rows = rows;
     j.cols = cols;
     j.ld = ld;
@@ -107,6 +111,7 @@ int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
                 st.occ_mask[b][M] = tsenor::occupancy_mask(M, b);
                 st.occ_round[b][M] = tsenor::occupancy_round(M, b);
                 st.occ_batched[b][M] = tsenor::occupancy_batched(M, b);
+                st.occ_refine[b][M] = tsenor::occupancy_refine(M, b);
             }
         st.init = true;
     }
@@ -158,16 +163,26 @@ extern "C" {
 int tsenor_mask(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,
                 float tau, int iters, int ls_steps, uint32_t* mask_out, float* frac_out,
                 void* stream) {
+    return tsenor_mask_ex(W, dtype, rows, cols, ld, N, M, tau, iters, ls_steps, 0, nullptr,
+                          mask_out, frac_out, stream);
+}
+
+int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N,
+                   int M, float tau, int iters, int ls_steps, int polish_steps,
+                   const uint32_t* prev_mask, uint32_t* mask_out, float* frac_out,
+                   void* stream) {
     int st_code = check_matrix(W, dtype, rows, cols, ld, N, M, mask_out);
     if (st_code != TSENOR_OK) return st_code;
     st_code = check_params(tau, iters, ls_steps);
     if (st_code != TSENOR_OK) return st_code;
+    if (polish_steps < 0) return TSENOR_ERR_PARAM;
 
     DeviceState* st = nullptr;
     std::unique_lock<std::mutex> lk;
     if ((st_code = acquire(&st, &lk)) != TSENOR_OK) return st_code;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, frac_out);
+    job.prev = prev_mask;
     const int64_t grid = clamp_grid(groups_of(job), st->num_cu, st->occ_mask[job.bf16][M]);
     if ((st_code = ensure_scratch(*st, (size_t)grid)) != TSENOR_OK) return st_code;
     Params prm;
@@ -175,9 +190,45 @@ int tsenor_mask(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld
     prm.iters = iters;
     prm.ls_steps = ls_steps;
     prm.scratch = st->scratch;
+    const bool refine = polish_steps > 0 || prev_mask != nullptr;
+    const size_t words = (size_t)rows * (size_t)job.wpr;
+    if (prev_mask != nullptr && prev_mask == mask_out && st->prev_cap < words) {
+        // the previous mask is overwritten by the solve: keep a copy
+        hipError_t e = hipSuccess;
+        if (st->prev_copy != nullptr) {
+            e = hipEventSynchronize(st->last);
+            if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+            (void)hipFree(st->prev_copy);
+            st->prev_copy = nullptr;
+            st->prev_cap = 0;
+        }
+        e = hipMalloc(&st->prev_copy, words * sizeof(uint32_t));
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(previous mask copy)");
+        st->prev_cap = words;
+    }
     if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
-    hipError_t e = (hipError_t)tsenor::launch_mask(job, prm, (int)grid, stream);
-    if (e != hipSuccess) return hip_fail(e, "mask kernel launch");
+    hipError_t e;
+    if (prev_mask != nullptr && prev_mask == mask_out) {
+        e = hipMemcpyAsync(st->prev_copy, prev_mask, words * sizeof(uint32_t),
+                           hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(previous mask)");
+        job.prev = st->prev_copy;
+    }
+    e = (hipError_t)tsenor::launch_mask(job, prm, (int)grid, stream);
+    if (e != hipSuccess) {
+        (void)record_end(*st, s);
+        return hip_fail(e, "mask kernel launch");
+    }
+    if (refine) {
+        const int64_t per_pass = tsenor::kWave / M;
+        const int64_t groups = (rows / M) * ((cols / M + per_pass - 1) / per_pass);
+        const int64_t rgrid = clamp_grid(groups, st->num_cu, st->occ_refine[job.bf16][M]);
+        e = (hipError_t)tsenor::launch_refine(job, polish_steps, (int)rgrid, stream);
+        if (e != hipSuccess) {
+            (void)record_end(*st, s);
+            return hip_fail(e, "refine kernel launch");
+        }
+    }
     return record_end(*st, s);
 }
 

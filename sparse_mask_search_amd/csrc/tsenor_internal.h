@@ -10,6 +10,7 @@ struct MatJob {
     const void* W;      // device, [rows][ld]
     uint32_t* mask;     // device, [rows][wpr]
     float* frac;        // device, [rows][cols] or nullptr
+    const uint32_t* prev;  // device, [rows][wpr] previous mask for the keep-better stage, or nullptr
     int64_t rows, cols, ld, wpr;
     int64_t group_begin;  // batched launch: first group id of this matrix within its (M, dtype) class
     int32_t N, M;
@@ -38,11 +39,15 @@ int blocks_per_group(int M);
 int launch_mask(const MatJob& job, const Params& prm, int grid, void* stream);
 int launch_round(const MatJob& job, const float* S, int64_t lds, int ls_steps, int grid,
                  void* stream);
+// Optional stages on job.mask in place: at most polish_steps 2-opt swaps per
+// block, then keep job.prev where it is feasible and better (if non-null).
+int launch_refine(const MatJob& job, int polish_steps, int grid, void* stream);
 int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int M, int bf16,
                    const Params& prm, int grid, void* stream);
 // Number of 64-lane workgroups of each kernel that fit on one CU at once.
 int occupancy_mask(int M, int bf16);
 int occupancy_round(int M, int bf16);
 int occupancy_batched(int M, int bf16);
+int occupancy_refine(int M, int bf16);
 
 }  // namespace tsenor

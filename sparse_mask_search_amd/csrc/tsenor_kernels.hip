@@ -1002,6 +1002,221 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     if (valid && bit0 == 0) job.mask[(br * M + i) * job.wpr + ((bc * M) >> 5)] = w;
 }
 
+// ---------------------------------------------------------------- refine
+// Optional stages on a finished mask (job.mask), for the 64/M blocks of one
+// pass: lane (q, i) = block q, row i.  |W| rows are staged in LDS like the
+// rounding's; the result is written back to job.mask.
+template <int M, bool BF16>
+__device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64_t bc, bool valid,
+                                            int polish_steps, float* __restrict__ lds) {
+    constexpr int G = kWave / M;
+    constexpr uint32_t FULL = kFull<M>;
+    int lane = threadIdx.x;
+    asm volatile("" : "+v"(lane));
+    const int q = lane / M, i = lane % M;
+    const int N = job.N;
+    float* Ss = lds;                                                     // scratch for R5
+    float* As = lds + G * kStageBlk<M>;                                  // [G][M][M+1]
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(As + G * M * (M + 1));  // [G][M]
+    uint32_t Z = 0u;
+    {
+        float a[M];
+        if (valid) {
+            load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, a);
+            const int64_t c0 = bc * M;
+            Z = (job.mask[(br * M + i) * job.wpr + (c0 >> 5)] >> (int)(c0 & 31)) & FULL;
+        } else {
+#pragma unroll
+            for (int j = 0; j < M; ++j) a[j] = 0.f;
+        }
+        float* Ai = As + (q * M + i) * (M + 1);
+#pragma unroll
+        for (int j = 0; j < M; ++j) Ai[j] = a[j];
+    }
+    __syncthreads();
+
+    // ---- R4: 2-opt polish (optional) ----
+    // A swap takes kept (i, j), (i', j'), i < i', with Z_ij' = Z_i'j = 0, to
+    // (i, j'), (i', j); gain fl(fl(A_ij' - A_i'j') + fl(A_i'j - A_ij)).  Per row
+    // pair the gain is monotone in each rounded difference, so the best gain
+    // is fl(T1 + T2) with T1 = max over j' of the first difference and T2 =
+    // max over j of the second; the smallest j and then j' attaining it give
+    // the lexicographic tie-break.
+    if (polish_steps > 0) {
+        // Pair table: the best swap of every row pair {a < b} of the block as a
+        // packed (fp32 gain, ~lexicographic index) key, 0 = none.  It is filled
+        // once; after a swap of rows r1, r2 only the pairs touching r1 or r2
+        // change, and lane p re-evaluates {p, r1} and {p, r2} -- two pairs per
+        // lane per step.
+        uint64_t* tab = reinterpret_cast<uint64_t*>(Zs + G * M) + q * M * M;  // [M][M], a < b
+        float ai[M];
+        {
+            const float* Ai = As + (q * M + i) * (M + 1);
+#pragma unroll
+            for (int c = 0; c < M; ++c) ai[c] = Ai[c];
+        }
+        Zs[q * M + i] = Z;
+        __syncthreads();
+        // Best swap of the pair {i, p} (p != i), row p's mask Zp: with a =
+        // min(i, p), b = max(i, p), d_c = fl(A_ac - A_bc) = +-fl(A_ic - A_pc),
+        // the second difference is fl(A_bj - A_aj) = -d_j exactly, so the best
+        // gain is fl(T1 - min over j of d_j), T1 = max over j' of d_j'.
+        auto pair_key = [&](int p, uint32_t Zp) -> uint64_t {
+            const bool lo = i < p;
+            const uint32_t Za = lo ? Z : Zp, Zb = lo ? Zp : Z;
+            const uint32_t dj = Za & ~Zb;   // j:  Z_aj = 1, Z_bj = 0
+            const uint32_t dk = Zb & ~Za;   // j': Z_bj' = 1, Z_aj' = 0
+            const float* Ap = As + (q * M + p) * (M + 1);
+            float T1 = -__builtin_inff(), Dmin = __builtin_inff();
+#pragma unroll
+            for (int c = 0; c < M; ++c) {
+                const float x = __fsub_rn(ai[c], Ap[c]);
+                const float d = lo ? x : -x;
+                if ((dk >> c) & 1u) T1 = fmaxf(T1, d);
+                if ((dj >> c) & 1u) Dmin = fminf(Dmin, d);
+            }
+            const float G = __fadd_rn(T1, -Dmin);
+            if (dj == 0u || !(G > 0.f)) return 0ull;
+            int jb = M;
+            float t2 = 0.f;
+#pragma unroll
+            for (int c = 0; c < M; ++c) {
+                const float x = __fsub_rn(ai[c], Ap[c]);
+                const float d = lo ? x : -x;
+                const bool hit = jb == M && ((dj >> c) & 1u) && __fadd_rn(T1, -d) == G;
+                jb = hit ? c : jb;
+                t2 = hit ? -d : t2;
+            }
+            int jpb = M;
+#pragma unroll
+            for (int c = 0; c < M; ++c) {
+                const float x = __fsub_rn(ai[c], Ap[c]);
+                const float d = lo ? x : -x;
+                const bool hit = jpb == M && ((dk >> c) & 1u) && __fadd_rn(d, t2) == G;
+                jpb = hit ? c : jpb;
+            }
+            const int a = lo ? i : p, b = lo ? p : i;
+            const uint32_t lex = (uint32_t)(((a * M + jb) * M + b) * M + jpb);
+            return ((uint64_t)float_to_ord(G) << 32) | (uint64_t)(0xFFFFFFFFu - lex);
+        };
+        // Fill: lane i takes the partners i+1 .. i+M/2 (mod M), the last one only
+        // for i < M/2 -- every pair exactly once, about M/2 pairs per lane.
+        for (int k = 1; k <= M / 2; ++k) {
+            const int p = (i + k) % M;
+            if (k < M / 2 || i < M / 2) {
+                const int a = i < p ? i : p, b = i < p ? p : i;
+                tab[a * M + b] = valid ? pair_key(p, Zs[q * M + p]) : 0ull;
+            }
+        }
+        __syncthreads();
+        bool active = valid;
+        for (int step = 0; step < polish_steps && __ballot(active) != 0ull; ++step) {
+            uint64_t best = 0;
+            for (int p = 1; p < M; ++p) {
+                if (p > i) {
+                    const uint64_t k = tab[i * M + p];
+                    best = k > best ? k : best;
+                }
+            }
+            if (!active) best = 0ull;
+            best = group_max_u64<M>(best);
+            __syncthreads();
+            int r1 = -1, r2 = -1;
+            if (active) {
+                if (best == 0ull) {
+                    active = false;  // no improving swap left in this block
+                } else {
+                    const uint32_t lex = 0xFFFFFFFFu - (uint32_t)best;
+                    const int jp = (int)(lex % M), ip = (int)((lex / M) % M);
+                    const int j = (int)((lex / (M * M)) % M), ii = (int)(lex / (M * M * M));
+                    if (i == ii) Z = (Z & ~(1u << j)) | (1u << jp);
+                    if (i == ip) Z = (Z & ~(1u << jp)) | (1u << j);
+                    Zs[q * M + i] = Z;
+                    r1 = ii;
+                    r2 = ip;
+                }
+            }
+            __syncthreads();
+            if (r1 >= 0) {
+                // lane i refreshes {i, r1} and {i, r2}; lane r1 refreshes {r1, r2}
+                const int pa = (i == r1) ? r2 : r1;
+                const int pb = (i == r1 || i == r2) ? -1 : r2;
+                {
+                    const int lo2 = i < pa ? i : pa, hi2 = i < pa ? pa : i;
+                    if (i != r2 || pa != r1) tab[lo2 * M + hi2] = pair_key(pa, Zs[q * M + pa]);
+                }
+                if (pb >= 0) {
+                    const int lo2 = i < pb ? i : pb, hi2 = i < pb ? pb : i;
+                    tab[lo2 * M + hi2] = pair_key(pb, Zs[q * M + pb]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- R5: keep the caller's previous mask where it is feasible and better ----
+    // Objective of a block: row sums over j ascending, then over rows i
+    // ascending, both in fp64 (every lane forms the same total from LDS).
+    if (job.prev != nullptr) {
+        const float* Ai = As + (q * M + i) * (M + 1);
+        uint32_t Zp = 0u;
+        if (valid) {
+            const int64_t c0 = bc * M;
+            Zp = (job.prev[(br * M + i) * job.wpr + (c0 >> 5)] >> (int)(c0 & 31)) & FULL;
+        }
+        const bool rows_ok = __popc(Zp) == N;
+        const bool cols_ok = __popc(transpose_bits<M>(Zp, (uint32_t)lane)) == N;
+        const uint64_t okb = __ballot(rows_ok && cols_ok);
+        const bool feasible = ((uint32_t)(okb >> (q * M)) & FULL) == FULL;
+        double rz = 0.0, rp = 0.0;
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            const double a = (double)Ai[j];
+            if ((Z >> j) & 1u) rz += a;
+            if ((Zp >> j) & 1u) rp += a;
+        }
+        double* sums = reinterpret_cast<double*>(Ss);  // [G][M][2]; staging area is free now
+        sums[2 * (q * M + i)] = rz;
+        sums[2 * (q * M + i) + 1] = rp;
+        __syncthreads();
+        double tz = 0.0, tp = 0.0;
+        for (int k = 0; k < M; ++k) {
+            tz += sums[2 * (q * M + k)];
+            tp += sums[2 * (q * M + k) + 1];
+        }
+        __syncthreads();
+        if (valid && feasible && tp > tz) Z = Zp;
+    }
+
+    // ---- store: OR the blocks of one 32-column word together ----
+    const int bit0 = (int)((bc * M) & 31);
+    uint32_t w = valid ? (Z << bit0) : 0u;
+    if constexpr (M <= 4) w |= xor_lane<4>(w);
+    if constexpr (M <= 8) w |= xor_lane<8>(w);
+    if constexpr (M <= 16) w |= xor_lane<16>(w);
+    if (valid && bit0 == 0) job.mask[(br * M + i) * job.wpr + ((bc * M) >> 5)] = w;
+}
+
+// Refine LDS: the rounding's staging areas, then the pair table of the polish
+// (M*M keys of 8 bytes per block).
+template <int M> constexpr int ref_lds_floats() {
+    return rnd_lds_floats<M>() + 2 * (kWave / M) * M * M + 2;
+}
+
+template <int M, bool BF16>
+__global__ __launch_bounds__(kWave) void refine_kernel(MatJob job, int polish_steps) {
+    __shared__ __attribute__((aligned(16))) float lds[ref_lds_floats<M>()];
+    constexpr int G = kWave / M;
+    const int64_t nbc = job.cols / M;
+    const int64_t gpr = (nbc + G - 1) / G;
+    const int64_t groups = (job.rows / M) * gpr;
+    for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
+        const int64_t br = g / gpr, bc = (g % gpr) * G + (int)threadIdx.x / M;
+        refine_pass<M, BF16>(job, br, bc, bc < nbc, polish_steps, lds);
+        __syncthreads();
+    }
+}
+
 // Whole path for group gl (block-row br, first block column bc0) of one matrix.
 template <int M, bool BF16>
 __device__ __forceinline__ void process_group(const MatJob& job, const Params& prm, int64_t gl,
@@ -1136,6 +1351,21 @@ int occupancy_round(int M, int bf16) {
     int n = 0;
     TSENOR_DISPATCH(M, bf16,
                     (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, round_kernel<MM, B>,
+                                                                       kWave, 0));
+    return n;
+}
+
+int launch_refine(const MatJob& job, int polish_steps, int grid, void* stream) {
+    TSENOR_DISPATCH(job.M, job.bf16,
+                    hipLaunchKernelGGL((refine_kernel<MM, B>), dim3(grid), dim3(kWave), 0,
+                                       (hipStream_t)stream, job, polish_steps));
+    return (int)hipGetLastError();
+}
+
+int occupancy_refine(int M, int bf16) {
+    int n = 0;
+    TSENOR_DISPATCH(M, bf16,
+                    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, refine_kernel<MM, B>,
                                                                        kWave, 0));
     return n;
 }

@@ -25,8 +25,8 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert names == ["tsenor_last_error", "tsenor_mask", "tsenor_mask_batched", "tsenor_round",
-                     "tsenor_status_str", "tsenor_version"]
+    assert names == ["tsenor_last_error", "tsenor_mask", "tsenor_mask_batched", "tsenor_mask_ex",
+                     "tsenor_round", "tsenor_status_str", "tsenor_version"]
     out = subprocess.check_output(["nm", "-D", "--defined-only", sms.library_path()], text=True)
     exported = set(re.findall(r"\bT (tsenor_\w+)", out))
     for n in names:
@@ -58,6 +58,19 @@ def _mask(W=FAKE, dtype=1, rows=64, cols=64, ld=64, N=2, M=4, tau=20.0, iters=10
 ])
 def test_mask_rejects(kw, code):
     assert _mask(**kw) == code
+
+
+def test_mask_ex_rejects():
+    """The extended entry point validates like tsenor_mask, plus polish_steps."""
+    l = sms.lib()
+    r = lambda W=FAKE, rows=64, N=2, ls=4, polish=0, prev=None, mask=FAKE: l.tsenor_mask_ex(
+        W, 1, rows, 64, 64, N, 4, 20.0, 10, ls, polish, prev, mask, None, None)
+    assert r(polish=-1) == PARAM
+    assert r(W=None, polish=3) == NULL
+    assert r(mask=None, prev=FAKE) == NULL
+    assert r(rows=66, polish=2) == SHAPE
+    assert r(N=7) == NM
+    assert r(ls=-2, prev=FAKE) == PARAM
 
 
 def test_round_rejects():

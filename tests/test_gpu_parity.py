@@ -321,3 +321,58 @@ def test_generic_scores(N, M, rows, cols):
     ref, _ = oracle.round_matrix(S, Sc, N, M, 12)
     assert np.array_equal(words(mask_t), ref)
     assert_feasible(words(mask_t), rows, cols, N, M)
+
+
+@pytest.mark.parametrize("polish", [2, 1000])
+@pytest.mark.parametrize("M,nbc,nbr", SMALL)
+def test_polish_parity(M, nbc, nbr, polish):
+    """Optional 2-opt polish after the fill: masks bit-exact with the oracle's
+    rounding (with the same polish) of the GPU's S, every block feasible and
+    never below the unpolished objective."""
+    import torch
+    N = M // 2
+    tau, iters, ls = 20.0, 60, 2
+    W_np = _small(500 + M, M, nbc, nbr, "student_t", M >= 16)
+    rows, cols = W_np.shape
+    _note(f"polish {polish} M={M} {rows}x{cols}")
+    W = to_device(W_np)
+    m1, S_t = sms.mask(W, N, M, tau, iters, ls, return_frac=True, polish_steps=polish)
+    m0 = sms.mask(W, N, M, tau, iters, ls)[0]
+    torch.cuda.synchronize()
+    S = S_t.cpu().numpy()
+    Wf = as_f32(W_np)
+    ref, st = oracle.round_matrix_ex(S, Wf, N, M, ls, polish)
+    assert np.array_equal(words(m1), ref)
+    assert_feasible(words(m1), rows, cols, N, M)
+    A = np.abs(Wf.astype(np.float64))
+    z1 = oracle.unpack_mask(words(m1), cols) * A
+    z0 = oracle.unpack_mask(words(m0), cols) * A
+    assert z1.sum() >= z0.sum() and st[4] > 0
+    print(f"polish {polish} M={M}: swaps {st[4]}, objective +{(z1.sum() / z0.sum() - 1):.3%}",
+          flush=True)
+
+
+@pytest.mark.parametrize("M,nbc,nbr", SMALL)
+def test_keep_better_previous_mask(M, nbc, nbr):
+    """A previous mask (here a polished one, with some blocks made infeasible)
+    is kept exactly where the oracle keeps it; in place (prev = out) gives the
+    same result."""
+    import torch
+    N = M // 2
+    tau, iters, ls = 20.0, 60, 2
+    W_np = _small(700 + M, M, nbc, nbr, "outlier", M == 8)
+    rows, cols = W_np.shape
+    _note(f"previous mask M={M} {rows}x{cols}")
+    W = to_device(W_np)
+    prev, _ = sms.mask(W, N, M, tau, iters, ls, polish_steps=50)
+    prev = prev.clone()
+    prev[::3, 0] ^= 1  # break row counts of some blocks: those must ignore it
+    m, S_t = sms.mask(W, N, M, tau, iters, ls, return_frac=True, prev_mask=prev)
+    inplace = prev.clone()
+    sms.mask(W, N, M, tau, iters, ls, out=inplace, prev_mask=inplace)
+    torch.cuda.synchronize()
+    ref, st = oracle.round_matrix_ex(S_t.cpu().numpy(), as_f32(W_np), N, M, ls, 0,
+                                     prev_mask=words(prev))
+    assert np.array_equal(words(m), ref) and np.array_equal(words(inplace), ref)
+    assert_feasible(words(m), rows, cols, N, M)
+    assert st[5] > 0
