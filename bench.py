@@ -219,6 +219,8 @@ def main():
     ap.add_argument("--workload", default="16:32-8192x28672-bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--polish-steps", type=int, default=0,
+                    help="add the optional 2-opt polish (at most this many swaps per block)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the method has no "
@@ -247,7 +249,7 @@ def main():
     torch.cuda.synchronize()
 
     def step():
-        sms.mask(W, w.N, w.M, w.tau, w.iters, w.ls_steps, out=out)
+        sms.mask(W, w.N, w.M, w.tau, w.iters, w.ls_steps, out=out, polish_steps=args.polish_steps)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -289,13 +291,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "N": w.N, "M": w.M, "rows": w.rows, "cols": w.cols,
                    "input_dtype": w.dtype, "tau": w.tau, "iters": w.iters,
-                   "ls_steps": w.ls_steps, "blocks": w.blocks, "recipe": w.recipe,
-                   "seed": w.seed},
+                   "ls_steps": w.ls_steps, "polish_steps": args.polish_steps,
+                   "blocks": w.blocks, "recipe": w.recipe, "seed": w.seed},
         "blocks_per_s": round(w.blocks / (ms_wall / 1e3), 1),
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_VALU_TOPS,
                      "unit": "Tops/s", "frac": round(achieved / PEAK_VALU_TOPS, 4),
-                     "traffic": measured_traffic(w.name),
-                     "kernel": "mask_kernel (gather + Dykstra + rounding + pack, one launch)",
+                     "traffic": measured_traffic(w.name) if args.polish_steps == 0 else None,
+                     "kernel": "mask_kernel (gather + Dykstra + rounding + pack, one launch)"
+                               + (" + refine_kernel" if args.polish_steps else ""),
                      "kernel_ms": round(ms, 4),
                      "ops_per_launch": ops,
                      "hbm_algorithmic_bytes": hbm_bytes,
