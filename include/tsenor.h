@@ -110,6 +110,27 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
                    const uint32_t* prev_mask, uint32_t* mask_out, float* frac_out,
                    void* stream);
 
+/* Exact optimum of every block: the mask with N ones per row and column that
+ * keeps the most |W| (the block LP is a bipartite b-matching, so its optimum
+ * is integral).  Not part of the method -- the reference it is measured
+ * against (optimality gap, speed-up over an exact solver).  From a feasible
+ * start, negative cycles of the block's residual graph are cancelled until a
+ * Bellman-Ford pass finds none, which certifies optimality up to 2^-40 of the
+ * block's max |W|.
+ *   start_mask  device, same layout as mask_out: a feasible start, e.g. the
+ *            output of tsenor_mask (blocks whose start is not feasible, and
+ *            every block when NULL, start from the circulant mask row i ->
+ *            columns i .. i+N-1 mod M).  May alias mask_out.
+ *   max_cancel  >= 0, cancellations allowed per block.
+ *   mask_out device, written entirely; always feasible.
+ *   objective_out  device, fp64 [rows/M][cols/M] per-block objective (sum of
+ *            |W| over the mask, rows then columns ascending), NaN where
+ *            optimality was not certified within max_cancel; or NULL.
+ * Other arguments, errors and conventions as in tsenor_mask.                   */
+int tsenor_exact(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,
+                 const uint32_t* start_mask, int max_cancel, uint32_t* mask_out,
+                 double* objective_out, void* stream);
+
 /* One matrix of a batch.  Field meanings as in tsenor_mask.                    */
 typedef struct {
     const void* W;

@@ -49,6 +49,8 @@ def lib():
         l.tsenor_mask_ex.argtypes = [_P, _I, _I64, _I64, _I64, _I, _I, _F, _I, _I, _I, _P, _P, _P,
                                      _P]
         l.tsenor_mask_ex.restype = _I
+        l.tsenor_exact.argtypes = [_P, _I, _I64, _I64, _I64, _I, _I, _P, _I, _P, _P, _P]
+        l.tsenor_exact.restype = _I
         l.tsenor_round.argtypes = [_P, _I64, _P, _I, _I64, _I64, _I64, _I, _I, _I, _P, _P]
         l.tsenor_round.restype = _I
         l.tsenor_mask_batched.argtypes = [ctypes.POINTER(_Matrix), _I, _F, _I, _I, _P]
@@ -144,6 +146,30 @@ def mask(W, N: int, M: int, tau: float, iters: int, ls_steps: int, return_frac: 
     if st != 0:
         raise TsenorError(st, "tsenor_mask_ex")
     return out, frac_out
+
+
+def exact(W, N: int, M: int, start=None, max_cancel: int = 4096, out=None,
+          return_objective: bool = False, stream=None):
+    """Exact optimum mask of every block (tsenor_exact).  start: a feasible
+    mask tensor to start from (e.g. the output of mask()), or None.  Returns
+    (mask, objective) with objective an fp64 [rows/M, cols/M] tensor of
+    per-block optima (NaN where not certified) if requested, else None."""
+    torch = _torch()
+    dt = _weights(W)
+    rows, cols = W.shape
+    out = _mask_buffer(W, out)
+    if start is not None:
+        start = _mask_buffer(W, start)
+    objv = (torch.empty((rows // M, cols // M), dtype=torch.float64, device=W.device)
+            if return_objective else None)
+    st = lib().tsenor_exact(ctypes.c_void_p(W.data_ptr()), dt, rows, cols, W.stride(0), N, M,
+                            ctypes.c_void_p(start.data_ptr() if start is not None else 0),
+                            int(max_cancel), ctypes.c_void_p(out.data_ptr()),
+                            ctypes.c_void_p(objv.data_ptr() if objv is not None else 0),
+                            _stream(stream))
+    if st != 0:
+        raise TsenorError(st, "tsenor_exact")
+    return out, objv
 
 
 def round_mask(S, W, N: int, M: int, ls_steps: int, out=None, stream=None):

@@ -43,6 +43,7 @@ struct DeviceState {
     int occ_round[2][33] = {};
     int occ_batched[2][33] = {};
     int occ_refine[2][33] = {};
+    int occ_exact[2][33] = {};
     uint32_t* prev_copy = nullptr;  // copy of a previous mask that aliases the output
     size_t prev_cap = 0;            // words
 };
@@ -112,6 +113,7 @@ int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
                 st.occ_round[b][M] = tsenor::occupancy_round(M, b);
                 st.occ_batched[b][M] = tsenor::occupancy_batched(M, b);
                 st.occ_refine[b][M] = tsenor::occupancy_refine(M, b);
+                st.occ_exact[b][M] = tsenor::occupancy_exact(M, b);
             }
         st.init = true;
     }
@@ -228,6 +230,29 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
             (void)record_end(*st, s);
             return hip_fail(e, "refine kernel launch");
         }
+    }
+    return record_end(*st, s);
+}
+
+int tsenor_exact(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,
+                 const uint32_t* start_mask, int max_cancel, uint32_t* mask_out,
+                 double* objective_out, void* stream) {
+    int st_code = check_matrix(W, dtype, rows, cols, ld, N, M, mask_out);
+    if (st_code != TSENOR_OK) return st_code;
+    if (max_cancel < 0) return TSENOR_ERR_PARAM;
+    DeviceState* st = nullptr;
+    std::unique_lock<std::mutex> lk;
+    if ((st_code = acquire(&st, &lk)) != TSENOR_OK) return st_code;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, nullptr);
+    const int64_t units = (rows / M) * job.wpr;
+    const int64_t grid = clamp_grid(units, st->num_cu, st->occ_exact[job.bf16][M]);
+    if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
+    hipError_t e = (hipError_t)tsenor::launch_exact(job, start_mask, objective_out, max_cancel,
+                                                    (int)grid, stream);
+    if (e != hipSuccess) {
+        (void)record_end(*st, s);
+        return hip_fail(e, "exact kernel launch");
     }
     return record_end(*st, s);
 }

@@ -42,6 +42,12 @@ int launch_round(const MatJob& job, const float* S, int64_t lds, int ls_steps, i
 // Optional stages on job.mask in place: at most polish_steps 2-opt swaps per
 // block, then keep job.prev where it is feasible and better (if non-null).
 int launch_refine(const MatJob& job, int polish_steps, int grid, void* stream);
+// Exact optimum of every block by negative-cycle canceling from `start` (a
+// feasible mask, or nullptr for a circulant start) into job.mask; per-block
+// objectives (fp64, NaN if not proven within max_cancel cancellations) to obj
+// when non-null.  One workgroup per (block-row, 32-column word).
+int launch_exact(const MatJob& job, const uint32_t* start, double* obj, int max_cancel, int grid,
+                 void* stream);
 int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int M, int bf16,
                    const Params& prm, int grid, void* stream);
 // Number of 64-lane workgroups of each kernel that fit on one CU at once.
@@ -49,5 +55,6 @@ int occupancy_mask(int M, int bf16);
 int occupancy_round(int M, int bf16);
 int occupancy_batched(int M, int bf16);
 int occupancy_refine(int M, int bf16);
+int occupancy_exact(int M, int bf16);
 
 }  // namespace tsenor

@@ -1217,6 +1217,216 @@ __global__ __launch_bounds__(kWave) void refine_kernel(MatJob job, int polish_st
     }
 }
 
+// ---------------------------------------------------------------- exact
+// Optimal mask of every block (the block LP -- rows and columns summing to N,
+// 0 <= S <= 1 -- is a bipartite b-matching, hence integral).  Starting from a
+// feasible mask, a mask is optimal iff the residual graph has no negative
+// cycle: row i -> column j for Z_ij = 0 at cost -|W_ij|, column j -> row i for
+// Z_ij = 1 at cost +|W_ij|.  Each round of Bellman-Ford from a virtual source
+// (all distances 0) relaxes every node's incoming arcs at once (one lane per
+// row or column node, fp64 distances); a change in round 2M proves a negative
+// cycle, which is found by following predecessors and cancelled (Z flips along
+// it, every row and column count is kept, the objective rises by -cost).  A
+// block is done when a Bellman-Ford pass settles; `tol` = 2^-40 * max|W| of the
+// block ignores cycles within rounding.  One wave handles one 32-column word
+// of one block-row (32/M blocks of 2M lanes).
+template <int M> __device__ __forceinline__ uint32_t circulant_row(int i, int N) {
+    uint32_t z = 0u;
+    for (int k = 0; k < N; ++k) z |= 1u << ((i + k) % M);
+    return z;
+}
+
+template <int M, bool BF16>
+__global__ __launch_bounds__(kWave) void exact_kernel(MatJob job, const uint32_t* __restrict__ start,
+                                                      double* __restrict__ obj, int max_cancel) {
+    constexpr int V = 2 * M, NB = kWave / V;
+    constexpr uint32_t FULL = kFull<M>;
+    static_assert(NB * M == 32, "one wave covers one 32-column word");
+    __shared__ double dist_s[kWave];
+    __shared__ int pred_s[kWave];
+    __shared__ uint32_t z_s[kWave];
+    __shared__ int cyc_s[NB][V + 1];
+    __shared__ double sum_s[kWave];
+    __shared__ float a_s[NB][M][M];  // the blocks' scores, for the cycle costs
+    constexpr uint64_t kBlkLanes = (V == 64) ? ~0ull : ((1ull << V) - 1ull);
+    const int lane = threadIdx.x;
+    const int b = lane / V, v = lane % V;
+    const bool isrow = v < M;
+    const int idx = isrow ? v : v - M;
+    const int N = job.N;
+    const int64_t nbc = job.cols / M, nbr = job.rows / M;
+    const int64_t units = nbr * job.wpr;
+    for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+        const int64_t br = u / job.wpr, w = u % job.wpr;
+        const int64_t bc = w * NB + b;
+        const bool valid = bc < nbc;
+        const int64_t r0 = br * M, c0 = bc * M;
+        // |W| along this node's row (row node) or column (column node)
+        double a[M];
+        double amax = 0.0;
+#pragma unroll
+        for (int k = 0; k < M; ++k) {
+            float x = 0.f;
+            if (valid) {
+                const int64_t off = isrow ? (r0 + idx) * job.ld + c0 + k : (r0 + k) * job.ld + c0 + idx;
+                if constexpr (BF16)
+                    x = __uint_as_float((uint32_t)(static_cast<const uint16_t*>(job.W)[off] & 0x7FFFu) << 16);
+                else
+                    x = fabsf(static_cast<const float*>(job.W)[off]);
+            }
+            a[k] = (double)x;
+            amax = fmax(amax, a[k]);
+        }
+        // start mask (row nodes read it; an infeasible start block falls back
+        // to the circulant mask row i -> columns i .. i+N-1 mod M)
+        uint32_t zr = 0u;
+        if (isrow && valid)
+            zr = start ? (start[(r0 + idx) * job.wpr + (c0 >> 5)] >> (int)(c0 & 31)) & FULL
+                       : circulant_row<M>(idx, N);
+        z_s[lane] = zr;
+        sum_s[lane] = amax;
+        __syncthreads();
+        uint32_t zc = 0u;  // column nodes: bit i = Z_i,idx
+#pragma unroll
+        for (int k = 0; k < M; ++k) zc |= ((z_s[b * V + k] >> idx) & 1u) << k;
+        double bmax = 0.0;
+#pragma unroll
+        for (int k = 0; k < V; ++k) bmax = fmax(bmax, sum_s[b * V + k]);
+        const double tol = bmax * 0x1p-40;
+        const bool cnt_ok = __popc(isrow ? zr : zc) == N;
+        const uint64_t okb = __ballot(cnt_ok);
+        const bool feasible = ((okb >> (b * V)) & kBlkLanes) == kBlkLanes;
+        __syncthreads();
+        if (!feasible) {
+            zr = (isrow && valid) ? circulant_row<M>(idx, N) : 0u;
+            z_s[lane] = zr;
+            __syncthreads();
+            zc = 0u;
+#pragma unroll
+            for (int k = 0; k < M; ++k) zc |= ((z_s[b * V + k] >> idx) & 1u) << k;
+            __syncthreads();
+        }
+        uint32_t z = isrow ? zr : zc;
+        if (isrow) {
+#pragma unroll
+            for (int k = 0; k < M; ++k) a_s[b][idx][k] = (float)a[k];
+        }
+        bool done = !valid;
+        bool failed = false;
+        for (int cancel = 0; cancel <= max_cancel && __ballot(!done) != 0ull; ++cancel) {
+            double d = 0.0;
+            int pred = -1;
+            bool settled = done, neg = false, last = false;
+            for (int round = 0; round <= V && __ballot(!settled) != 0ull; ++round) {
+                dist_s[lane] = d;
+                __syncthreads();
+                double best = d;
+                int bp = -1;
+                if (!settled) {
+#pragma unroll
+                    for (int k = 0; k < M; ++k) {
+                        // row node: arcs column k -> row idx for Z_idx,k = 1 (cost +A);
+                        // column node: arcs row k -> column idx for Z_k,idx = 0 (cost -A)
+                        const bool arc = isrow ? ((z >> k) & 1u) != 0u : ((z >> k) & 1u) == 0u;
+                        const double c = isrow ? dist_s[b * V + M + k] + a[k] : dist_s[b * V + k] - a[k];
+                        if (arc && c < best - tol) {
+                            best = c;
+                            bp = isrow ? M + k : k;
+                        }
+                    }
+                }
+                __syncthreads();
+                const bool ch = bp >= 0;
+                if (ch) { d = best; pred = bp; }
+                const uint64_t chb = __ballot(ch);
+                const bool blk_ch = ((chb >> (b * V)) & kBlkLanes) != 0ull;
+                if (!settled && !blk_ch) settled = true;
+                if (!settled && round == V) {
+                    neg = true;
+                    settled = true;
+                    last = ch;  // changed in the last round: its predecessors lead into a cycle
+                }
+            }
+            pred_s[lane] = pred;
+            z_s[lane] = last ? 1u : 0u;
+            __syncthreads();
+            if (neg && v == 0) {
+                // walk the predecessors onto the cycle, list it (cyc_s[b][0] =
+                // length, then the nodes; pred(x) follows x) and check its cost
+                int x = -1;
+                for (int k = 0; k < V; ++k)
+                    if (z_s[b * V + k] != 0u) { x = k; break; }
+                bool ok = x >= 0;
+                for (int t = 0; t < V && ok; ++t) {
+                    x = pred_s[b * V + x];
+                    ok = x >= 0;
+                }
+                int n = 0;
+                double cost = 0.0;
+                if (ok) {
+                    const int s0 = x;
+                    do {
+                        const int y = pred_s[b * V + x];
+                        cyc_s[b][1 + n] = x;
+                        ++n;
+                        if (y < 0) break;
+                        cost += (y < M) ? -(double)a_s[b][y][x - M] : (double)a_s[b][x][y - M];
+                        x = y;
+                    } while (x != s0 && n < V);
+                    ok = x == s0 && (n & 1) == 0 && cost < -tol;
+                }
+                cyc_s[b][0] = ok ? n : -1;
+            }
+            __syncthreads();
+            if (neg) {
+                const int n = cyc_s[b][0];
+                if (n < 0) {
+                    done = true;  // no usable cycle (rounding): keep the current mask
+                    failed = true;
+                } else {
+                    for (int t = 0; t < n; ++t) {  // arc y -> x with y = pred(x)
+                        const int x = cyc_s[b][1 + t];
+                        const int y = cyc_s[b][1 + (t + 1) % n];
+                        if (y < M && x >= M) {  // row y -> column x: Z_y,x 0 -> 1
+                            if (isrow && idx == y) z |= 1u << (x - M);
+                            if (!isrow && idx == x - M) z |= 1u << y;
+                        } else if (y >= M && x < M) {  // column y -> row x: Z_x,y 1 -> 0
+                            if (isrow && idx == x) z &= ~(1u << (y - M));
+                            if (!isrow && idx == y - M) z &= ~(1u << x);
+                        }
+                    }
+                    if (cancel == max_cancel) { done = true; failed = true; }
+                }
+            } else {
+                done = true;  // no negative cycle: optimal
+            }
+            __syncthreads();
+        }
+        // store: row lanes OR their blocks' bits into the word of their row
+        z_s[lane] = (isrow && valid) ? (z << (b * M)) : 0u;
+        double rs = 0.0;
+        if (isrow) {
+#pragma unroll
+            for (int k = 0; k < M; ++k)
+                if ((z >> k) & 1u) rs += a[k];
+        }
+        sum_s[lane] = rs;
+        __syncthreads();
+        if (b == 0 && isrow) {
+            uint32_t word = 0u;
+#pragma unroll
+            for (int q = 0; q < NB; ++q) word |= z_s[q * V + idx];
+            if (br * M + idx < job.rows && w < job.wpr) job.mask[(r0 + idx) * job.wpr + w] = word;
+        }
+        if (obj != nullptr && valid && v == 0) {
+            double tot = 0.0;
+            for (int k = 0; k < M; ++k) tot += sum_s[b * V + k];
+            obj[br * nbc + bc] = failed ? __builtin_nan("") : tot;
+        }
+        __syncthreads();
+    }
+}
+
 // Whole path for group gl (block-row br, first block column bc0) of one matrix.
 template <int M, bool BF16>
 __device__ __forceinline__ void process_group(const MatJob& job, const Params& prm, int64_t gl,
@@ -1360,6 +1570,22 @@ int launch_refine(const MatJob& job, int polish_steps, int grid, void* stream) {
                     hipLaunchKernelGGL((refine_kernel<MM, B>), dim3(grid), dim3(kWave), 0,
                                        (hipStream_t)stream, job, polish_steps));
     return (int)hipGetLastError();
+}
+
+int launch_exact(const MatJob& job, const uint32_t* start, double* obj, int max_cancel, int grid,
+                 void* stream) {
+    TSENOR_DISPATCH(job.M, job.bf16,
+                    hipLaunchKernelGGL((exact_kernel<MM, B>), dim3(grid), dim3(kWave), 0,
+                                       (hipStream_t)stream, job, start, obj, max_cancel));
+    return (int)hipGetLastError();
+}
+
+int occupancy_exact(int M, int bf16) {
+    int n = 0;
+    TSENOR_DISPATCH(M, bf16,
+                    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, exact_kernel<MM, B>,
+                                                                       kWave, 0));
+    return n;
 }
 
 int occupancy_refine(int M, int bf16) {

@@ -25,8 +25,8 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert names == ["tsenor_last_error", "tsenor_mask", "tsenor_mask_batched", "tsenor_mask_ex",
-                     "tsenor_round", "tsenor_status_str", "tsenor_version"]
+    assert names == ["tsenor_exact", "tsenor_last_error", "tsenor_mask", "tsenor_mask_batched",
+                     "tsenor_mask_ex", "tsenor_round", "tsenor_status_str", "tsenor_version"]
     out = subprocess.check_output(["nm", "-D", "--defined-only", sms.library_path()], text=True)
     exported = set(re.findall(r"\bT (tsenor_\w+)", out))
     for n in names:
@@ -71,6 +71,17 @@ def test_mask_ex_rejects():
     assert r(rows=66, polish=2) == SHAPE
     assert r(N=7) == NM
     assert r(ls=-2, prev=FAKE) == PARAM
+
+
+def test_exact_rejects():
+    l = sms.lib()
+    r = lambda W=FAKE, rows=64, N=2, M=4, mc=10, mask=FAKE: l.tsenor_exact(
+        W, 0, rows, 64, 64, N, M, None, mc, mask, None, None)
+    assert r(W=None) == NULL
+    assert r(mask=None) == NULL
+    assert r(mc=-1) == PARAM
+    assert r(rows=63) == SHAPE
+    assert r(M=7) == NM
 
 
 def test_round_rejects():

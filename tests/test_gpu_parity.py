@@ -376,3 +376,52 @@ def test_keep_better_previous_mask(M, nbc, nbr):
     assert np.array_equal(words(m), ref) and np.array_equal(words(inplace), ref)
     assert_feasible(words(m), rows, cols, N, M)
     assert st[5] > 0
+
+
+@pytest.mark.parametrize("M,N,nbc,nbr,kind", [
+    (4, 2, 70, 3, "student_t"), (8, 3, 45, 2, "outlier"), (16, 8, 37, 2, "student_t"),
+    (16, 5, 21, 2, "ties"), (32, 16, 19, 2, "outlier"), (32, 7, 9, 1, "student_t")])
+def test_exact_matches_oracle_optimum(M, N, nbc, nbr, kind):
+    """tsenor_exact from the method's mask and from the circulant start: every
+    block's objective equals the oracle's min-cost-flow optimum (fp64, 1e-9
+    relative), the mask is feasible and realises that objective, and it is
+    never below the method's mask."""
+    import torch
+    W_np = _small(900 + M + N, M, nbc, nbr, kind, M >= 16)
+    rows, cols = W_np.shape
+    _note(f"exact M={M} N={N} {rows}x{cols} {kind}")
+    W = to_device(W_np)
+    Wf = as_f32(W_np)
+    m0, _ = sms.mask(W, N, M, 20.0, 60, 4)
+    ids = np.arange((rows // M) * (cols // M))
+    opt = oracle.exact_opt_blocks(Wf, N, M, ids)
+    A = np.abs(Wf.astype(np.float64))
+    for start in (m0, None):
+        m, objv = sms.exact(W, N, M, start=start, return_objective=True)
+        torch.cuda.synchronize()
+        mw = words(m)
+        assert_feasible(mw, rows, cols, N, M)
+        o = objv.cpu().numpy().ravel()
+        assert np.isfinite(o).all()
+        assert np.allclose(o, opt, rtol=1e-9, atol=1e-12), np.abs(o - opt).max()
+        got = (oracle.block_view(oracle.unpack_mask(mw, cols).astype(np.float64), M)
+               * oracle.block_view(A, M)).sum((2, 3)).ravel()
+        assert np.allclose(got, opt, rtol=1e-9, atol=1e-12)
+    base = (oracle.block_view(oracle.unpack_mask(words(m0), cols).astype(np.float64), M)
+            * oracle.block_view(A, M)).sum((2, 3)).ravel()
+    assert (opt >= base - 1e-9).all()
+    print(f"exact M={M} N={N}: method's mean gap {np.mean((opt - base) / opt):.4%}", flush=True)
+
+
+def test_exact_cancel_limit():
+    """With no cancellations allowed the circulant start is returned where it is
+    not already optimal, flagged NaN; the mask stays feasible."""
+    import torch
+    M, N = 8, 3
+    W_np = _small(1234, M, 20, 2, "student_t", False)
+    rows, cols = W_np.shape
+    W = to_device(W_np)
+    m, objv = sms.exact(W, N, M, max_cancel=0, return_objective=True)
+    torch.cuda.synchronize()
+    assert_feasible(words(m), rows, cols, N, M)
+    assert np.isnan(objv.cpu().numpy()).any()
