@@ -131,6 +131,37 @@ int tsenor_exact(const void* W, int dtype, int64_t rows, int64_t cols, int64_t l
                  const uint32_t* start_mask, int max_cancel, uint32_t* mask_out,
                  double* objective_out, void* stream);
 
+/* ---- 2:4 consumer: one transposable mask serves W and W^T ----------------
+ * Not part of the mask search: the payoff the pages measure -- with a 2:4
+ * transposable mask (N = 2, M = 4) both the forward product Y = X W^T and the
+ * data gradient dX = dY W = dY (W^T)^T reduce over a 2:4-sparse dimension and
+ * run on the sparse matrix cores.
+ *
+ * Compressed operand A [arows][k], 2:4 along k (k a multiple of 32):
+ *   values  device bf16 [arows][k/2]: per aligned group of 4 along k, its kept
+ *           entries (at most two) in ascending position, unused slots 0;
+ *   meta    device uint32 [arows][k/32]: group g of each 32-wide chunk in bits
+ *           4g..4g+3, low two bits = position of the first value, high two =
+ *           the second's.
+ *
+ * tsenor_compress24: A = W (transpose 0: arows = rows, k = cols) or A = W^T
+ * (transpose 1: arows = cols, k = rows) restricted to `mask` (the layout of
+ * tsenor_mask's output).  W is bf16 [rows][ld].  Groups with more than two
+ * kept entries keep the first two and are counted into *bad_groups (device
+ * int, added to; NULL = no count).  Errors: NULL pointers, bad shapes
+ * (k % 32 != 0), transpose not 0/1.
+ *
+ * tsenor_spmm24: Y = X A^T.  X device bf16 [n][ldx] (16-byte aligned, ldx a
+ * multiple of 8), A compressed [m][k], Y device fp32 [n][ldy] (16-byte
+ * aligned, ldy a multiple of 4), fp32 accumulation.  n and m multiples of 128,
+ * k of 32 (TSENOR_ERR_SHAPE otherwise).  Asynchronous on `stream`.          */
+int tsenor_compress24(const void* W, int64_t rows, int64_t cols, int64_t ld,
+                      const uint32_t* mask, int transpose, uint16_t* values_out,
+                      uint32_t* meta_out, int* bad_groups, void* stream);
+int tsenor_spmm24(const void* X, int64_t n, int64_t ldx, const uint16_t* values,
+                  const uint32_t* meta, int64_t m, int64_t k, float* Y, int64_t ldy,
+                  void* stream);
+
 /* One matrix of a batch.  Field meanings as in tsenor_mask.                    */
 typedef struct {
     const void* W;

@@ -241,3 +241,53 @@ def block_view(X: np.ndarray, M: int) -> np.ndarray:
     """[rows, cols] -> [rows/M, cols/M, M, M] (copy)."""
     r, c = X.shape
     return X.reshape(r // M, M, c // M, M).transpose(0, 2, 1, 3).copy()
+
+
+# --------------------------------------------------------------------------
+# 2:4 compressed operand (the consumer of transposable masks; format as in
+# include/tsenor.h's tsenor_compress24 -- restated here from its definition).
+
+def compress24(W_bits, mask_words, transpose: bool = False):
+    """A = W (or W^T) restricted to the mask, compressed 2:4 along its rows.
+    W_bits: uint16 bf16 bit patterns [rows, cols]; mask_words: uint32 packed
+    mask.  Returns (values uint16 [arows, k/2], meta uint32 [arows, k/32],
+    groups with more than two kept entries)."""
+    W_bits = np.asarray(W_bits, dtype=np.uint16)
+    rows, cols = W_bits.shape
+    Z = unpack_mask(np.asarray(mask_words, dtype=np.uint32), cols)
+    A, ZA = (W_bits.T, Z.T) if transpose else (W_bits, Z)
+    arows, k = A.shape
+    if k % 32:
+        raise ValueError("k must be a multiple of 32")
+    vals = np.zeros((arows, k // 2), np.uint16)
+    meta = np.zeros((arows, k // 32), np.uint32)
+    bad = 0
+    for r in range(arows):
+        for g in range(k // 4):
+            pos = [j for j in range(4) if ZA[r, 4 * g + j]]
+            bad += len(pos) > 2
+            pos = pos[:2]
+            if len(pos) == 0:
+                code = 0 | (1 << 2)
+            elif len(pos) == 1:
+                code = pos[0] | ((2 if pos[0] == 3 else 3) << 2)
+            else:
+                code = pos[0] | (pos[1] << 2)
+            for s_, p in enumerate(pos):
+                vals[r, 2 * g + s_] = A[r, 4 * g + p]
+            meta[r, g // 8] |= np.uint32(code << (4 * (g % 8)))
+    return vals, meta, bad
+
+
+def decompress24(vals, meta, k: int):
+    """Dense fp32 [arows, k] from the compressed operand (unused slots are 0)."""
+    vals = np.asarray(vals, dtype=np.uint16)
+    arows = vals.shape[0]
+    out = np.zeros((arows, k), np.float32)
+    f = (vals.astype(np.uint32) << 16).view(np.float32)
+    for r in range(arows):
+        for g in range(k // 4):
+            code = (int(meta[r, g // 8]) >> (4 * (g % 8))) & 0xF
+            for s_, p in enumerate((code & 3, code >> 2)):
+                out[r, 4 * g + p] += f[r, 2 * g + s_]
+    return out

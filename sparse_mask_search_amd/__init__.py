@@ -14,8 +14,8 @@ Transposable N:M Sparse Masks" (arXiv 2505.23949), "What carries the argument".
 """
 from __future__ import annotations
 
-from ._lib import (F32, BF16, TsenorError, exact, lib, library_path, mask, mask_batched,
-                   round_mask, unpack, version)
+from ._lib import (F32, BF16, TsenorError, compress24, exact, lib, library_path, mask,
+                   mask_batched, round_mask, spmm24, unpack, version)
 
-__all__ = ["F32", "BF16", "TsenorError", "exact", "lib", "library_path", "mask", "mask_batched",
-           "round_mask", "unpack", "version"]
+__all__ = ["F32", "BF16", "TsenorError", "compress24", "exact", "lib", "library_path", "mask",
+           "mask_batched", "round_mask", "spmm24", "unpack", "version"]

@@ -51,6 +51,10 @@ def lib():
         l.tsenor_mask_ex.restype = _I
         l.tsenor_exact.argtypes = [_P, _I, _I64, _I64, _I64, _I, _I, _P, _I, _P, _P, _P]
         l.tsenor_exact.restype = _I
+        l.tsenor_compress24.argtypes = [_P, _I64, _I64, _I64, _P, _I, _P, _P, _P, _P]
+        l.tsenor_compress24.restype = _I
+        l.tsenor_spmm24.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I64, _P, _I64, _P]
+        l.tsenor_spmm24.restype = _I
         l.tsenor_round.argtypes = [_P, _I64, _P, _I, _I64, _I64, _I64, _I, _I, _I, _P, _P]
         l.tsenor_round.restype = _I
         l.tsenor_mask_batched.argtypes = [ctypes.POINTER(_Matrix), _I, _F, _I, _I, _P]
@@ -170,6 +174,54 @@ def exact(W, N: int, M: int, start=None, max_cancel: int = 4096, out=None,
     if st != 0:
         raise TsenorError(st, "tsenor_exact")
     return out, objv
+
+
+def compress24(W, mask_words, transpose: bool = False, stream=None):
+    """2:4 compressed operand A = W (or W^T) under a 2:4 mask (tsenor_compress24).
+    W: bf16 CUDA tensor [rows, cols]; mask_words: the int32 mask of mask().
+    Returns (values bf16 [arows, k/2], meta int32 [arows, k/32], bad) with bad
+    a CUDA int32 tensor holding the number of groups with more than two kept
+    entries."""
+    torch = _torch()
+    if W.dtype != torch.bfloat16 or not W.is_cuda or W.dim() != 2 or W.stride(1) != 1:
+        raise TypeError("W must be a 2-D bfloat16 CUDA tensor with unit column stride")
+    rows, cols = W.shape
+    _mask_buffer(W, mask_words)
+    arows, k = (cols, rows) if transpose else (rows, cols)
+    vals = torch.empty((arows, k // 2), dtype=torch.bfloat16, device=W.device)
+    meta = torch.empty((arows, max(1, k // 32)), dtype=torch.int32, device=W.device)
+    bad = torch.zeros(1, dtype=torch.int32, device=W.device)
+    st = lib().tsenor_compress24(ctypes.c_void_p(W.data_ptr()), rows, cols, W.stride(0),
+                                 ctypes.c_void_p(mask_words.data_ptr()), int(bool(transpose)),
+                                 ctypes.c_void_p(vals.data_ptr()), ctypes.c_void_p(meta.data_ptr()),
+                                 ctypes.c_void_p(bad.data_ptr()), _stream(stream))
+    if st != 0:
+        raise TsenorError(st, "tsenor_compress24")
+    return vals, meta, bad
+
+
+def spmm24(X, values, meta, out=None, stream=None):
+    """Y = X A^T on the sparse matrix cores (tsenor_spmm24).  X: bf16 CUDA
+    tensor [n, k]; values/meta from compress24 (A is [m, k]).  Returns fp32
+    [n, m]."""
+    torch = _torch()
+    if X.dtype != torch.bfloat16 or not X.is_cuda or X.dim() != 2 or X.stride(1) != 1:
+        raise TypeError("X must be a 2-D bfloat16 CUDA tensor with unit column stride")
+    n, k = X.shape
+    m = values.shape[0]
+    if values.shape[1] * 2 != k or meta.shape != (m, k // 32) or not values.is_contiguous() \
+            or not meta.is_contiguous():
+        raise ValueError("compressed operand does not match X")
+    if out is None:
+        out = torch.empty((n, m), dtype=torch.float32, device=X.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (n, m) or out.stride(1) != 1:
+        raise ValueError(f"out must be a float32 tensor of shape {(n, m)} with unit column stride")
+    st = lib().tsenor_spmm24(ctypes.c_void_p(X.data_ptr()), n, X.stride(0),
+                             ctypes.c_void_p(values.data_ptr()), ctypes.c_void_p(meta.data_ptr()),
+                             m, k, ctypes.c_void_p(out.data_ptr()), out.stride(0), _stream(stream))
+    if st != 0:
+        raise TsenorError(st, "tsenor_spmm24")
+    return out
 
 
 def round_mask(S, W, N: int, M: int, ls_steps: int, out=None, stream=None):

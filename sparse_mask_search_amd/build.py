@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtsenor.so")
-SOURCES = ["tsenor_abi.cpp", "tsenor_kernels.hip"]
+SOURCES = ["tsenor_abi.cpp", "tsenor_kernels.hip", "tsenor_spmm.hip"]
 ARCH = os.environ.get("TSENOR_OFFLOAD_ARCH", "gfx950")
 
 

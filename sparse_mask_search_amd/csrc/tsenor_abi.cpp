@@ -257,6 +257,37 @@ int tsenor_exact(const void* W, int dtype, int64_t rows, int64_t cols, int64_t l
     return record_end(*st, s);
 }
 
+int tsenor_compress24(const void* W, int64_t rows, int64_t cols, int64_t ld,
+                      const uint32_t* mask, int transpose, uint16_t* values_out,
+                      uint32_t* meta_out, int* bad_groups, void* stream) {
+    if (W == nullptr || mask == nullptr || values_out == nullptr || meta_out == nullptr)
+        return TSENOR_ERR_NULL;
+    if (transpose != 0 && transpose != 1) return TSENOR_ERR_PARAM;
+    if (rows <= 0 || cols <= 0 || ld < cols || rows > (int64_t(1) << 40) / ld) return TSENOR_ERR_SHAPE;
+    const int64_t arows = transpose ? cols : rows, k = transpose ? rows : cols;
+    if (k % 32 != 0) return TSENOR_ERR_SHAPE;
+    const int64_t wpr = (cols + 31) / 32;
+    hipError_t e = (hipError_t)tsenor::launch_compress24(
+        static_cast<const uint16_t*>(W), ld, mask, wpr, arows, k, transpose, values_out, meta_out,
+        bad_groups, stream);
+    return e == hipSuccess ? TSENOR_OK : hip_fail(e, "compress24 kernel launch");
+}
+
+int tsenor_spmm24(const void* X, int64_t n, int64_t ldx, const uint16_t* values,
+                  const uint32_t* meta, int64_t m, int64_t k, float* Y, int64_t ldy,
+                  void* stream) {
+    if (X == nullptr || values == nullptr || meta == nullptr || Y == nullptr) return TSENOR_ERR_NULL;
+    if (n <= 0 || m <= 0 || k <= 0 || n % 128 != 0 || m % 128 != 0 || k % 32 != 0 || ldx < k ||
+        ldy < m || ldx % 8 != 0 || ldy % 4 != 0)
+        return TSENOR_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(X) & 15u) != 0 || (reinterpret_cast<uintptr_t>(Y) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(values) & 7u) != 0 || (reinterpret_cast<uintptr_t>(meta) & 3u) != 0)
+        return TSENOR_ERR_SHAPE;
+    hipError_t e = (hipError_t)tsenor::launch_spmm24(static_cast<const uint16_t*>(X), ldx, values,
+                                                     meta, Y, ldy, n, m, k, stream);
+    return e == hipSuccess ? TSENOR_OK : hip_fail(e, "spmm24 kernel launch");
+}
+
 int tsenor_round(const float* S, int64_t lds, const void* W, int dtype, int64_t rows,
                  int64_t cols, int64_t ld, int N, int M, int ls_steps, uint32_t* mask_out,
                  void* stream) {

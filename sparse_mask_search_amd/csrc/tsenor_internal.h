@@ -57,4 +57,11 @@ int occupancy_batched(int M, int bf16);
 int occupancy_refine(int M, int bf16);
 int occupancy_exact(int M, int bf16);
 
+// 2:4 consumer (tsenor_spmm.hip).
+int launch_compress24(const uint16_t* W, int64_t ld, const uint32_t* mask, int64_t wpr,
+                      int64_t rows, int64_t k, int trans, uint16_t* vals, uint32_t* meta, int* bad,
+                      void* stream);
+int launch_spmm24(const uint16_t* X, int64_t ldx, const uint16_t* vals, const uint32_t* meta,
+                  float* Y, int64_t ldy, int64_t n, int64_t m, int64_t k, void* stream);
+
 }  // namespace tsenor

@@ -1,0 +1,178 @@
+// tsenor_spmm.hip -- a consumer of transposable 2:4 masks on gfx950: the
+// weight matrix compressed to 2:4 along either of its dimensions, and
+// Y = X A^T on the sparse matrix cores (v_smfmac_f32_32x32x32_bf16).
+//
+// Why transposable masks matter (pith.science review of "TSENOR: Highly-
+// Efficient Algorithm for Finding Transposable N:M Sparse Masks", "Core
+// claim"): with one mask both W (forward, Y = X W^T) and W^T (data gradient,
+// dX = dY W = dY (W^T)^T) are 2:4 along the reduction dimension, so both
+// products run on the sparse matrix cores.
+//
+// Compressed operand A [rows][k] (2:4 along k):
+//   values  bf16 [rows][k/2]: for each aligned group of 4 along k, its (at most
+//           two) kept entries in ascending position; unused slots are 0.
+//   meta    uint32 [rows][k/32]: group g of a 32-wide chunk in bits 4g..4g+3,
+//           low two bits = position (0..3) of the first value, high two = the
+//           second's.
+// smfmac 32x32x32 operand layout (measured on gfx950 with an in-bounds probe):
+// lane l holds A row l%32, and for h = l/32 the groups 2h, 2h+1 (k = 8h..8h+7)
+// and 4+2h, 5+2h (k = 16+8h..16+8h+7) of the chunk, two slots per group with a
+// 2-bit position each in the index operand; B lane l holds column l%32 at
+// k = 16h..16h+15; the accumulator is the usual 32x32 layout (lane l: column
+// l%32, rows 8*i0 + 4h + i1).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tsenor_internal.h"
+
+namespace tsenor {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One thread per (row of A, 32-wide chunk of k): element (r, c) of A is
+// W[r][c] (trans = 0) or W[c][r] (trans = 1); mask bit likewise.  Groups with
+// more than two kept entries are counted into *bad (their first two are kept).
+__global__ void compress24_kernel(const uint16_t* __restrict__ W, int64_t ld,
+                                  const uint32_t* __restrict__ mask, int64_t wpr, int64_t rows,
+                                  int64_t k, int trans, uint16_t* __restrict__ vals,
+                                  uint32_t* __restrict__ meta, int* __restrict__ bad) {
+    const int64_t chunks = k / 32;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= rows * chunks) return;
+    const int64_t r = t / chunks, ch = t % chunks;
+    uint32_t mw = 0u;
+    uint16_t v[16];
+    int nbad = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        int cnt = 0;
+        uint32_t pos = 0u;
+        uint16_t x0 = 0, x1 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t c = ch * 32 + 4 * g + j;
+            const int64_t wr = trans ? c : r, wc = trans ? r : c;
+            const bool keep = (mask[wr * wpr + (wc >> 5)] >> (int)(wc & 31)) & 1u;
+            if (keep) {
+                const uint16_t x = W[wr * ld + wc];
+                if (cnt == 0) { x0 = x; pos |= (uint32_t)j; }
+                else if (cnt == 1) { x1 = x; pos |= (uint32_t)j << 2; }
+                ++cnt;
+            }
+        }
+        if (cnt > 2) ++nbad;
+        if (cnt < 2) {  // pad: the unused slot points at a free position, value 0
+            const uint32_t p0 = pos & 3u;
+            if (cnt == 0) pos = 0u | (1u << 2);
+            else pos = p0 | ((p0 == 3u ? 2u : 3u) << 2);
+        }
+        v[2 * g] = x0;
+        v[2 * g + 1] = x1;
+        mw |= pos << (4 * g);
+    }
+    uint16_t* out = vals + r * (k / 2) + ch * 16;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) out[q] = v[q];
+    meta[r * chunks + ch] = mw;
+    if (nbad && bad != nullptr) atomicAdd(bad, nbad);
+}
+
+// Y [n][m] fp32 (leading dimension ldy) = X [n][k] bf16 (ldx) times A^T, A
+// [m][k] compressed as above.  One workgroup of 4 waves per 128 x 128 tile of
+// (m, n); each wave owns 64 x 64 = 2 x 2 smfmac tiles and walks k in chunks of
+// 32.  m, n multiples of 128 and k of 32 (checked on the host).
+__global__ __launch_bounds__(256) void spmm24_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                     const uint16_t* __restrict__ vals,
+                                                     const uint32_t* __restrict__ meta,
+                                                     float* __restrict__ Y, int64_t ldy, int64_t n,
+                                                     int64_t m, int64_t k) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int64_t tiles_m = m / 128;
+    const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    const int64_t m0 = tm * 128 + 64 * (wave >> 1), n0 = tn * 128 + 64 * (wave & 1);
+    const int64_t chunks = k / 32;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) acc[a][b][t] = 0.f;
+    const uint16_t* arow[2];
+    const uint32_t* mrow[2];
+    const uint16_t* brow[2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+        const int64_t r = m0 + 32 * a + l32;
+        arow[a] = vals + r * (k / 2) + 4 * h;
+        mrow[a] = meta + r * chunks;
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) brow[b] = X + (n0 + 32 * b + l32) * ldx + 16 * h;
+    for (int64_t ch = 0; ch < chunks; ++ch) {
+        bf16x8 av[2];
+        int idx[2];
+        bf16x16 bv[2];
+#pragma unroll
+        for (int a = 0; a < 2; ++a) {
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(arow[a] + ch * 16);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(arow[a] + ch * 16 + 8);
+            const u32x4 w4 = {lo.x, lo.y, hi.x, hi.y};
+            av[a] = __builtin_bit_cast(bf16x8, w4);
+            const uint32_t mw = mrow[a][ch];
+            idx[a] = (int)(((mw >> (8 * h)) & 0xFFu) | (((mw >> (16 + 8 * h)) & 0xFFu) << 8));
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const u32x4 p = *reinterpret_cast<const u32x4*>(brow[b] + ch * 32);
+            const u32x4 q = *reinterpret_cast<const u32x4*>(brow[b] + ch * 32 + 8);
+            typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+            const u32x8 w8 = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+            bv[b] = __builtin_bit_cast(bf16x16, w8);
+        }
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(av[a], bv[b], acc[a][b], idx[a], 0, 0);
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            float* y = Y + (n0 + 32 * b + l32) * ldy + m0 + 32 * a + 4 * h;
+#pragma unroll
+            for (int i0 = 0; i0 < 4; ++i0)
+                *reinterpret_cast<float4*>(y + 8 * i0) =
+                    make_float4(acc[a][b][4 * i0], acc[a][b][4 * i0 + 1], acc[a][b][4 * i0 + 2],
+                                acc[a][b][4 * i0 + 3]);
+        }
+}
+
+}  // namespace
+
+int launch_compress24(const uint16_t* W, int64_t ld, const uint32_t* mask, int64_t wpr,
+                      int64_t rows, int64_t k, int trans, uint16_t* vals, uint32_t* meta, int* bad,
+                      void* stream) {
+    const int64_t threads = rows * (k / 32);
+    const int64_t blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL(compress24_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       W, ld, mask, wpr, rows, k, trans, vals, meta, bad);
+    return (int)hipGetLastError();
+}
+
+int launch_spmm24(const uint16_t* X, int64_t ldx, const uint16_t* vals, const uint32_t* meta,
+                  float* Y, int64_t ldy, int64_t n, int64_t m, int64_t k, void* stream) {
+    const int64_t blocks = (m / 128) * (n / 128);
+    hipLaunchKernelGGL(spmm24_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, X,
+                       ldx, vals, meta, Y, ldy, n, m, k);
+    return (int)hipGetLastError();
+}
+
+}  // namespace tsenor

@@ -25,8 +25,9 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert names == ["tsenor_exact", "tsenor_last_error", "tsenor_mask", "tsenor_mask_batched",
-                     "tsenor_mask_ex", "tsenor_round", "tsenor_status_str", "tsenor_version"]
+    assert names == ["tsenor_compress24", "tsenor_exact", "tsenor_last_error", "tsenor_mask",
+                     "tsenor_mask_batched", "tsenor_mask_ex", "tsenor_round", "tsenor_spmm24",
+                     "tsenor_status_str", "tsenor_version"]
     out = subprocess.check_output(["nm", "-D", "--defined-only", sms.library_path()], text=True)
     exported = set(re.findall(r"\bT (tsenor_\w+)", out))
     for n in names:
@@ -82,6 +83,23 @@ def test_exact_rejects():
     assert r(mc=-1) == PARAM
     assert r(rows=63) == SHAPE
     assert r(M=7) == NM
+
+
+def test_spmm24_rejects():
+    l = sms.lib()
+    c = lambda W=FAKE, rows=64, cols=64, ld=64, mask=FAKE, tr=0, v=FAKE, m=FAKE: l.tsenor_compress24(
+        W, rows, cols, ld, mask, tr, v, m, None, None)
+    assert c(W=None) == NULL and c(v=None) == NULL and c(mask=None) == NULL
+    assert c(tr=2) == PARAM
+    assert c(cols=48, ld=48) == SHAPE          # k = 48 not a multiple of 32
+    assert c(rows=48, tr=1) == SHAPE
+    assert c(ld=32) == SHAPE
+    s = lambda X=FAKE, n=128, ldx=64, v=FAKE, meta=FAKE, m=128, k=64, Y=FAKE, ldy=128: \
+        l.tsenor_spmm24(X, n, ldx, v, meta, m, k, Y, ldy, None)
+    assert s(X=None) == NULL and s(Y=None) == NULL
+    assert s(n=96) == SHAPE and s(m=64) == SHAPE and s(k=48, ldx=48) == SHAPE
+    assert s(ldx=60, k=32) == SHAPE and s(ldy=100) == SHAPE
+    assert s(X=ctypes.c_void_p(0x1008)) == SHAPE  # misaligned
 
 
 def test_round_rejects():
