@@ -124,6 +124,11 @@ template <int M> constexpr int lds_floats() {
 }
 
 template <int M> constexpr uint32_t kFull = (M == 32) ? 0xFFFFFFFFu : ((1u << M) - 1u);
+// Waves per SIMD the solve+round kernels are built for.  The register budget
+// of the fused path sits close to these steps (512 / waves registers per
+// lane); pinning the target makes the allocator fit it rather than silently
+// drop a wave when unrelated code changes.
+template <int M> constexpr int kSolveWaves = (M <= 4) ? 8 : (M == 8) ? 4 : (M == 16) ? 3 : 2;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
@@ -341,7 +346,11 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                                               int64_t bc0, float* __restrict__ slot,
                                               float* __restrict__ lds) {
     constexpr int R = kR<M>, H = kH<M>, CW = kCW<M>, L = kL<M>;
-    const int lane = threadIdx.x;
+    // M = 32: an opaque lane, so that addresses derived from it are rebuilt
+    // per group instead of being hoisted out of the kernel's group loop, where
+    // they would stay live (and cost registers) through the whole solve.
+    int lane = threadIdx.x;
+    if constexpr (M >= 32) asm volatile("" : "+v"(lane));
     const int blk = lane / L, lb = lane % L;
     int g = lb / H, h = lb % H;
     if constexpr (kBfly<M>) { g = Lanes32::g(lb); h = Lanes32::h(lb); }
@@ -771,6 +780,19 @@ __device__ __forceinline__ int sum_step(int v) {
 }
 template <int M>
 __device__ __forceinline__ int group_sum(int v) { return sum_step<1, M>(v); }
+template <int S, int M, bool MAX>
+__device__ __forceinline__ uint32_t ext_u32_step(uint32_t v) {
+    if constexpr (S >= M) {
+        return v;
+    } else {
+        const uint32_t o = xor_lane<S>(v);
+        return ext_u32_step<2 * S, M, MAX>(MAX ? (o > v ? o : v) : (o < v ? o : v));
+    }
+}
+template <int M>
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t v) { return ext_u32_step<1, M, true>(v); }
+template <int M>
+__device__ __forceinline__ uint32_t group_min_u32(uint32_t v) { return ext_u32_step<1, M, false>(v); }
 
 // Greedy over the (S desc, index asc) order, as the fixed point of the row
 // and column thresholds; returns row i of the accepted mask.
@@ -906,51 +928,171 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
 
         int moves = 0;
         bool active = need && ls_steps > 0;
-        while (__ballot(active) != 0ull) {  // R2
-            uint64_t best = 0;
-            if (active) {
-                for (uint32_t dr = DR; dr; dr &= dr - 1u) {
-                    const int ii = __ffs(dr) - 1;
-                    const uint32_t cand0 = Z & ~Zs[q * M + ii];
-                    if (!cand0) continue;
-                    const float* Aii = As + (q * M + ii) * (M + 1);
-                    for (uint32_t dc = DC; dc; dc &= dc - 1u) {
-                        const int jj = __ffs(dc) - 1;
-                        if ((Z >> jj) & 1u) continue;
-                        const float a2 = Ai[jj];
-                        for (uint32_t cs = cand0; cs; cs &= cs - 1u) {
-                            const int jp = __ffs(cs) - 1;
-                            const float sc = __fsub_rn(__fadd_rn(Aii[jp], a2), Ai[jp]);
-                            const uint32_t lex = (uint32_t)(((ii * M + jj) * M + i) * M + jp);
-                            const uint64_t key =
-                                ((uint64_t)float_to_ord(sc) << 32) | (uint64_t)(0xFFFFFFFFu - lex);
-                            best = key > best ? key : best;
+        // R2: at most ls_steps moves, each the best (i, j, i', j') with a
+        // positive score, ties to the smallest in lexicographic order.
+        if constexpr (M <= 8) {
+            // Small blocks: a direct scan of every candidate, one packed
+            // (score, ~lexicographic index) maximum per step.
+            while (__ballot(active) != 0ull) {
+                uint64_t best = 0;
+                if (active) {
+                    for (uint32_t dr = DR; dr; dr &= dr - 1u) {
+                        const int ii = __ffs(dr) - 1;
+                        const uint32_t cand0 = Z & ~Zs[q * M + ii];
+                        if (!cand0) continue;
+                        const float* Aii = As + (q * M + ii) * (M + 1);
+                        for (uint32_t dc = DC; dc; dc &= dc - 1u) {
+                            const int jj = __ffs(dc) - 1;
+                            if ((Z >> jj) & 1u) continue;
+                            const float a2 = Ai[jj];
+                            for (uint32_t cs = cand0; cs; cs &= cs - 1u) {
+                                const int jp = __ffs(cs) - 1;
+                                const float sc = __fsub_rn(__fadd_rn(Aii[jp], a2), Ai[jp]);
+                                const uint32_t lex = (uint32_t)(((ii * M + jj) * M + i) * M + jp);
+                                const uint64_t key =
+                                    ((uint64_t)float_to_ord(sc) << 32) | (uint64_t)(0xFFFFFFFFu - lex);
+                                best = key > best ? key : best;
+                            }
                         }
                     }
                 }
-            }
-            best = group_max_u64<M>(best);
-            __syncthreads();
-            if (active) {
-                const float sc = ord_to_float((uint32_t)(best >> 32));
-                if (best == 0ull || !(sc > 0.f)) {
-                    active = false;
-                } else {
-                    const uint32_t lex = 0xFFFFFFFFu - (uint32_t)best;
-                    const int jp = (int)(lex % M), ip = (int)((lex / M) % M);
-                    const int jj = (int)((lex / (M * M)) % M), ii = (int)(lex / (M * M * M));
-                    if (i == ii) { Z |= 1u << jp; r += 1; }
-                    if (i == ip) Z = (Z | (1u << jj)) & ~(1u << jp);
-                    if (i == jj) c += 1;
-                    Zs[q * M + i] = Z;
-                    ++moves;
-                    --D;
-                    if (D == 0 || moves >= ls_steps) active = false;
+                best = group_max_u64<M>(best);
+                __syncthreads();
+                if (active) {
+                    const float sc = ord_to_float((uint32_t)(best >> 32));
+                    if (best == 0ull || !(sc > 0.f)) {
+                        active = false;
+                    } else {
+                        const uint32_t lex = 0xFFFFFFFFu - (uint32_t)best;
+                        const int jp = (int)(lex % M), ip = (int)((lex / M) % M);
+                        const int jj = (int)((lex / (M * M)) % M), ii = (int)(lex / (M * M * M));
+                        if (i == ii) { Z |= 1u << jp; r += 1; }
+                        if (i == ip) Z = (Z | (1u << jj)) & ~(1u << jp);
+                        if (i == jj) c += 1;
+                        Zs[q * M + i] = Z;
+                        ++moves;
+                        --D;
+                        if (D == 0 || moves >= ls_steps) active = false;
+                    }
                 }
+                __syncthreads();
+                DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
+                DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
             }
-            __syncthreads();
-            DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
-            DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
+        } else {
+            float* Cm = Ss + q * M;  // column maxima of block q (the staging area is free now)
+            // The score fl(fl(A_ij' + A_i'j) - A_i'j') is monotone in A_ij' and
+            // in A_i'j, and the admissibility of i (deficient, Z_ij' = 0) does not
+            // involve j, nor that of j (deficient, Z_i'j = 0) i.  So for a fixed
+            // (i', j') the best score takes the largest admissible A_ij' of column
+            // j' and the largest admissible A_i'j of row i'.  Lane i acts as column
+            // j' = i for the first maximum and as row i' = i for the second and for
+            // its best score.  The smallest (i, j, i', j') attaining the block's best
+            // score G is then found one coordinate at a time, each stage keeping
+            // only the candidates that can still reach G.
+            while (__ballot(active) != 0ull) {
+                float cmax = 0.f, rmax = 0.f;
+                bool hc = false, hr = false;
+                if (active) {
+                    for (uint32_t dr = DR; dr; dr &= dr - 1u) {
+                        const int ii = __ffs(dr) - 1;
+                        if ((Zs[q * M + ii] >> i) & 1u) continue;
+                        const float a = As[(q * M + ii) * (M + 1) + i];
+                        cmax = (!hc || a > cmax) ? a : cmax;
+                        hc = true;
+                    }
+                    for (uint32_t dc = DC & ~Z; dc; dc &= dc - 1u) {
+                        const float a = Ai[__ffs(dc) - 1];
+                        rmax = (!hr || a > rmax) ? a : rmax;
+                        hr = true;
+                    }
+                    Cm[i] = cmax;
+                }
+                const uint32_t CM = (uint32_t)(__ballot(hc) >> shift) & FULL;
+                __syncthreads();
+                uint32_t sk = 0u;  // ordered key of the lane's best score, 0 = no candidate
+                uint32_t J = 0u;   // the columns j' attaining it
+                if (active && hr) {
+                    for (uint32_t cs = Z & CM; cs; cs &= cs - 1u) {
+                        const int jp = __ffs(cs) - 1;
+                        const uint32_t k = float_to_ord(__fsub_rn(__fadd_rn(Cm[jp], rmax), Ai[jp]));
+                        J = (k > sk) ? (1u << jp) : (k == sk ? (J | (1u << jp)) : J);
+                        sk = k > sk ? k : sk;
+                    }
+                }
+                const uint32_t gk = group_max_u32<M>(sk);
+                const float Gs = ord_to_float(gk);
+                if (active && (gk == 0u || !(Gs > 0.f))) active = false;
+                if (sk != gk || !active) J = 0u;
+                // stage 1: smallest deficient row i
+                uint32_t t = M;
+                if (J) {
+                    for (uint32_t dr = DR; dr && t == (uint32_t)M; dr &= dr - 1u) {
+                        const int ii = __ffs(dr) - 1;
+                        const float* Aii = As + (q * M + ii) * (M + 1);
+                        for (uint32_t cs = J & ~Zs[q * M + ii]; cs; cs &= cs - 1u) {
+                            const int jp = __ffs(cs) - 1;
+                            if (__fsub_rn(__fadd_rn(Aii[jp], rmax), Ai[jp]) == Gs) {
+                                t = (uint32_t)ii;
+                                break;
+                            }
+                        }
+                    }
+                }
+                const int bi = (int)group_min_u32<M>(t);
+                // stage 2: smallest deficient column j for that row
+                uint32_t Jw = 0u;
+                t = M;
+                if (J && bi < M) {
+                    const float* Abi = As + (q * M + bi) * (M + 1);
+                    for (uint32_t cs = J & ~Zs[q * M + bi]; cs; cs &= cs - 1u) {
+                        const int jp = __ffs(cs) - 1;
+                        if (__fsub_rn(__fadd_rn(Abi[jp], rmax), Ai[jp]) == Gs) Jw |= 1u << jp;
+                    }
+                    for (uint32_t dc = DC & ~Z; dc && Jw && t == (uint32_t)M; dc &= dc - 1u) {
+                        const int jj = __ffs(dc) - 1;
+                        const float a2 = Ai[jj];
+                        for (uint32_t cs = Jw; cs; cs &= cs - 1u) {
+                            const int jp = __ffs(cs) - 1;
+                            if (__fsub_rn(__fadd_rn(Abi[jp], a2), Ai[jp]) == Gs) {
+                                t = (uint32_t)jj;
+                                break;
+                            }
+                        }
+                    }
+                }
+                const int bj = (int)group_min_u32<M>(t);
+                // stage 3: smallest row i', then its smallest column j'
+                uint32_t Jf = 0u;
+                if (Jw && bj < M && !((Z >> bj) & 1u)) {
+                    const float* Abi = As + (q * M + bi) * (M + 1);
+                    const float a2 = Ai[bj];
+                    for (uint32_t cs = Jw; cs; cs &= cs - 1u) {
+                        const int jp = __ffs(cs) - 1;
+                        if (__fsub_rn(__fadd_rn(Abi[jp], a2), Ai[jp]) == Gs) Jf |= 1u << jp;
+                    }
+                }
+                const uint32_t IP = (uint32_t)(__ballot(Jf != 0u) >> shift) & FULL;
+                const int bip = IP ? __ffs(IP) - 1 : M;
+                const int bjp = (int)group_max_u32<M>(i == bip ? (uint32_t)(__ffs(Jf) - 1) : 0u);
+                __syncthreads();
+                if (active) {
+                    if (bip >= M) {
+                        active = false;  // unreachable: G is attained by construction
+                    } else {
+                        if (i == bi) { Z |= 1u << bjp; r += 1; }
+                        if (i == bip) Z = (Z | (1u << bj)) & ~(1u << bjp);
+                        if (i == bj) c += 1;
+                        Zs[q * M + i] = Z;
+                        ++moves;
+                        --D;
+                        if (D == 0 || moves >= ls_steps) active = false;
+                    }
+                }
+                __syncthreads();
+                DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
+                DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
+            }
         }
         active = valid && D > 0;
         while (__ballot(active) != 0ull) {  // R3
@@ -1447,7 +1589,8 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
 }
 
 template <int M, bool BF16>
-__global__ __launch_bounds__(kWave) void mask_kernel(MatJob job, Params prm) {
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kSolveWaves<M>)))
+void mask_kernel(MatJob job, Params prm) {
     __shared__ __attribute__((aligned(16))) float lds[lds_floats<M>()];
     constexpr int BPG = kBPG<M>;
     const int64_t nbc = job.cols / M;
@@ -1480,8 +1623,8 @@ __global__ __launch_bounds__(kWave) void round_kernel(MatJob job, const float* _
 // grid walks the concatenated group range.  One kernel per class keeps the
 // register allocation of each path as tight as in mask_kernel.
 template <int M, bool BF16>
-__global__ __launch_bounds__(kWave) void batched_kernel(const MatJob* __restrict__ jobs, int count,
-                                                        int64_t total_groups, Params prm) {
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kSolveWaves<M>)))
+void batched_kernel(const MatJob* __restrict__ jobs, int count, int64_t total_groups, Params prm) {
     __shared__ __attribute__((aligned(16))) float lds[lds_floats<M>()];
     float* slot = prm.scratch + (int64_t)blockIdx.x * kSlotFloats;
     for (int64_t g = blockIdx.x; g < total_groups; g += gridDim.x) {

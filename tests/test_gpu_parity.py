@@ -91,6 +91,51 @@ def test_large_tau(M, nbc, nbr, tau):
     assert_feasible(mask, rows, cols, N, M)
 
 
+@pytest.mark.parametrize("iters", [1, 3])
+@pytest.mark.parametrize("kind", ["student_t", "ties"])
+@pytest.mark.parametrize("M,nbc,nbr", SMALL)
+def test_local_search_heavy(M, nbc, nbr, kind, iters):
+    """One or three Dykstra cycles leave S far from a transport plan: the
+    greedy falls short in most blocks and the local search makes many moves,
+    over tied scores too (the 'ties' weights take three magnitudes), so every
+    stage of its lexicographic tie-break decides some moves."""
+    N = M // 2
+    ls = M * M
+    W_np = _small(500 + M, M, nbc, nbr, kind, M >= 16)
+    rows, cols = W_np.shape
+    _note(f"heavy LS M={M} {rows}x{cols} {kind} iters={iters}")
+    _, mask, S, mask2 = _run(W_np, N, M, 20.0, iters, ls)
+    ref, stats = oracle.round_matrix(S, as_f32(W_np), N, M, ls)
+    print(f"M={M} {kind} T={iters}: shortfall blocks {stats[0]}, R2 moves {stats[2]}, "
+          f"R3 moves {stats[3]}", flush=True)
+    assert stats[2] > 0
+    assert np.array_equal(mask, ref) and np.array_equal(mask2, ref)
+    assert_feasible(mask, rows, cols, N, M)
+
+
+@pytest.mark.parametrize("ls", [1, 7, 1024])
+@pytest.mark.parametrize("M", [4, 8, 16, 32])
+def test_round_tied_scores(M, ls):
+    """Rounding alone on S with four levels and |W| with three: ties in the
+    sort order and in the swap scores everywhere; the move limit cuts the
+    search early (1, 7) or never (1024)."""
+    import torch
+    rng = np.random.default_rng(900 + M + ls)
+    N = M // 2
+    nbc, nbr = 41, 2
+    W_np = np.concatenate([wl.random_blocks(900 + M + r, nbc, M, "ties") for r in range(nbr)])
+    S_np = (rng.integers(0, 4, W_np.shape) / 4.0).astype(np.float32)
+    rows, cols = W_np.shape
+    _note(f"tied round M={M} {rows}x{cols} ls={ls}")
+    got = sms.round_mask(to_device(S_np), to_device(W_np), N, M, ls)
+    torch.cuda.synchronize()
+    ref, stats = oracle.round_matrix(S_np, W_np, N, M, ls)
+    print(f"M={M} ls={ls}: R2 moves {stats[2]}, R3 moves {stats[3]}", flush=True)
+    assert stats[2] > 0
+    assert np.array_equal(words(got), ref)
+    assert_feasible(words(got), rows, cols, N, M)
+
+
 @pytest.mark.parametrize("M,N", [(4, 1), (8, 3), (16, 5), (32, 7), (32, 31), (16, 16)])
 def test_other_n(M, N):
     W_np = _small(7 + N, M, 11, 2, "student_t", True)
