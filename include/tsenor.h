@@ -44,6 +44,12 @@
  *   - Results are deterministic: the same inputs give bit-identical masks and
  *     S on every run and for every stream.  Non-finite weights give undefined
  *     (but memory-safe) results.
+ *   - Debug checks: with the environment variable TSENOR_DEBUG_CHECKS=1 (read
+ *     at every call), tsenor_mask, tsenor_mask_ex, tsenor_mask_batched,
+ *     tsenor_round and tsenor_exact first count the non-finite elements of
+ *     their W (and S) on the device, wait for the count, and return
+ *     TSENOR_ERR_NONFINITE without launching anything else if it is not zero.
+ *     The wait synchronises `stream`, so such calls cannot be graph-captured.
  *   - The library keeps one cached device workspace per device (allocated on
  *     first use, grown on demand, never freed before process exit).  Calls on
  *     one device share it: each launch is ordered after the previous one on
@@ -68,7 +74,8 @@ typedef enum {
     TSENOR_ERR_NM = 3,    /* M not in {4, 8, 16, 32}, or N < 1, or N > M                 */
     TSENOR_ERR_PARAM = 4, /* tau not finite or < 0, iters < 1, ls_steps < 0, count < 0   */
     TSENOR_ERR_DTYPE = 5, /* dtype not a tsenor_dtype                                   */
-    TSENOR_ERR_HIP = 6    /* HIP runtime or launch failure                              */
+    TSENOR_ERR_HIP = 6,   /* HIP runtime or launch failure                              */
+    TSENOR_ERR_NONFINITE = 7 /* debug checks only: W (or S) holds an Inf or NaN          */
 } tsenor_status;
 
 /* Whole method (steps 1-3 above) on one matrix.

@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -46,6 +47,8 @@ struct DeviceState {
     int occ_exact[2][33] = {};
     uint32_t* prev_copy = nullptr;  // copy of a previous mask that aliases the output
     size_t prev_cap = 0;            // words
+    int* dbg_count = nullptr;       // debug checks: device counter and its pinned host copy
+    int* dbg_host = nullptr;
 };
 DeviceState g_dev[kMaxDevices];
 
@@ -158,6 +161,43 @@ int record_end(DeviceState& st, hipStream_t s) {
     return e == hipSuccess ? TSENOR_OK : hip_fail(e, "hipEventRecord");
 }
 
+// TSENOR_DEBUG_CHECKS=1 (read at every call): inputs are scanned for
+// non-finite values on the device before anything else is launched, and the
+// call waits for the answer (so it cannot be captured into a graph).
+bool debug_checks() {
+    const char* v = std::getenv("TSENOR_DEBUG_CHECKS");
+    return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+int check_finite(DeviceState& st, hipStream_t s, const void* p, int bf16, int64_t rows,
+                 int64_t cols, int64_t ld) {
+    hipError_t e;
+    if (st.dbg_count == nullptr) {
+        e = hipMalloc(&st.dbg_count, sizeof(int));
+        if (e != hipSuccess) {
+            st.dbg_count = nullptr;
+            return hip_fail(e, "hipMalloc(debug counter)");
+        }
+    }
+    if (st.dbg_host == nullptr) {
+        e = hipHostMalloc(reinterpret_cast<void**>(&st.dbg_host), sizeof(int), hipHostMallocDefault);
+        if (e != hipSuccess) {
+            st.dbg_host = nullptr;
+            return hip_fail(e, "hipHostMalloc(debug counter)");
+        }
+    }
+    const int64_t n = rows * cols;
+    const int64_t cap = (int64_t)st.num_cu * 8;
+    const int64_t grid = (n + 255) / 256 < cap ? (n + 255) / 256 : cap;
+    e = (hipError_t)tsenor::launch_count_nonfinite(p, bf16, rows, cols, ld, st.dbg_count, (int)grid, s);
+    if (e != hipSuccess) return hip_fail(e, "debug check launch");
+    e = hipMemcpyAsync(st.dbg_host, st.dbg_count, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(debug counter)");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(debug check)");
+    return *st.dbg_host != 0 ? TSENOR_ERR_NONFINITE : TSENOR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,6 +223,9 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
     std::unique_lock<std::mutex> lk;
     if ((st_code = acquire(&st, &lk)) != TSENOR_OK) return st_code;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_checks() &&
+        (st_code = check_finite(*st, s, W, dtype == TSENOR_BF16, rows, cols, ld)) != TSENOR_OK)
+        return st_code;
     MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, frac_out);
     job.prev = prev_mask;
     const int64_t grid = clamp_grid(groups_of(job), st->num_cu, st->occ_mask[job.bf16][M]);
@@ -244,6 +287,9 @@ int tsenor_exact(const void* W, int dtype, int64_t rows, int64_t cols, int64_t l
     std::unique_lock<std::mutex> lk;
     if ((st_code = acquire(&st, &lk)) != TSENOR_OK) return st_code;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_checks() &&
+        (st_code = check_finite(*st, s, W, dtype == TSENOR_BF16, rows, cols, ld)) != TSENOR_OK)
+        return st_code;
     MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, nullptr);
     const int64_t units = (rows / M) * job.wpr;
     const int64_t grid = clamp_grid(units, st->num_cu, st->occ_exact[job.bf16][M]);
@@ -301,6 +347,10 @@ int tsenor_round(const float* S, int64_t lds, const void* W, int dtype, int64_t 
     std::unique_lock<std::mutex> lk;
     if ((st_code = acquire(&st, &lk)) != TSENOR_OK) return st_code;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_checks() &&
+        ((st_code = check_finite(*st, s, W, dtype == TSENOR_BF16, rows, cols, ld)) != TSENOR_OK ||
+         (st_code = check_finite(*st, s, S, 0, rows, cols, lds)) != TSENOR_OK))
+        return st_code;
     MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, nullptr);
     const int64_t per_pass = tsenor::kWave / M;
     const int64_t nbc = cols / M;
@@ -308,7 +358,10 @@ int tsenor_round(const float* S, int64_t lds, const void* W, int dtype, int64_t 
     const int64_t grid = clamp_grid(groups, st->num_cu, st->occ_round[job.bf16][M]);
     if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
     hipError_t e = (hipError_t)tsenor::launch_round(job, S, lds, ls_steps, (int)grid, stream);
-    if (e != hipSuccess) return hip_fail(e, "round kernel launch");
+    if (e != hipSuccess) {
+        (void)record_end(*st, s);
+        return hip_fail(e, "round kernel launch");
+    }
     return record_end(*st, s);
 }
 
@@ -329,6 +382,12 @@ int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int ite
     std::unique_lock<std::mutex> lk;
     if ((st_code = acquire(&st, &lk)) != TSENOR_OK) return st_code;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (debug_checks())
+        for (int i = 0; i < count; ++i) {
+            const tsenor_matrix& m = mats[i];
+            st_code = check_finite(*st, s, m.W, m.dtype == TSENOR_BF16, m.rows, m.cols, m.ld);
+            if (st_code != TSENOR_OK) return st_code;
+        }
     hipError_t e;
     if (st->jobs_cap < (size_t)count) {
         if (st->jobs_dev != nullptr) {
@@ -408,6 +467,7 @@ const char* tsenor_status_str(int status) {
         case TSENOR_ERR_PARAM: return "bad parameter (tau finite >= 0, iters >= 1, ls_steps >= 0)";
         case TSENOR_ERR_DTYPE: return "bad dtype (TSENOR_F32 or TSENOR_BF16)";
         case TSENOR_ERR_HIP: return "HIP runtime error (see tsenor_last_error)";
+        case TSENOR_ERR_NONFINITE: return "input holds a non-finite value (TSENOR_DEBUG_CHECKS=1)";
         default: return "unknown status";
     }
 }

@@ -56,6 +56,10 @@ int occupancy_round(int M, int bf16);
 int occupancy_batched(int M, int bf16);
 int occupancy_refine(int M, int bf16);
 int occupancy_exact(int M, int bf16);
+// Writes to *count (device) the number of non-finite elements of a row-major
+// fp32 / bf16 matrix; two launches on `stream`.
+int launch_count_nonfinite(const void* p, int bf16, int64_t rows, int64_t cols, int64_t ld,
+                           int* count, int grid, void* stream);
 
 // 2:4 consumer (tsenor_spmm.hip).
 int launch_compress24(const uint16_t* W, int64_t ld, const uint32_t* mask, int64_t wpr,

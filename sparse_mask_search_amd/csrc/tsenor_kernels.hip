@@ -1638,6 +1638,30 @@ void batched_kernel(const MatJob* __restrict__ jobs, int count, int64_t total_gr
     }
 }
 
+// ---------------------------------------------------------------- debug check
+// Counts the non-finite elements of a row-major [rows][cols] matrix (leading
+// dimension ld), fp32 or bf16: those with an all-ones exponent field.
+__global__ __launch_bounds__(64) void zero_count_kernel(int* count) { *count = 0; }
+
+__global__ __launch_bounds__(256) void nonfinite_kernel(const void* __restrict__ p, int bf16,
+                                                        int64_t rows, int64_t cols, int64_t ld,
+                                                        int* __restrict__ count) {
+    const int64_t n = rows * cols;
+    int bad = 0;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = t / cols, c = t % cols;
+        if (bf16) {
+            const uint16_t u = static_cast<const uint16_t*>(p)[r * ld + c];
+            bad += (u & 0x7F80u) == 0x7F80u;
+        } else {
+            const uint32_t u = __float_as_uint(static_cast<const float*>(p)[r * ld + c]);
+            bad += (u & 0x7F800000u) == 0x7F800000u;
+        }
+    }
+    if (bad) atomicAdd(count, bad);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- host side
@@ -1745,6 +1769,14 @@ int occupancy_batched(int M, int bf16) {
                     (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, batched_kernel<MM, B>,
                                                                        kWave, 0));
     return n;
+}
+
+int launch_count_nonfinite(const void* p, int bf16, int64_t rows, int64_t cols, int64_t ld,
+                           int* count, int grid, void* stream) {
+    hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, count);
+    hipLaunchKernelGGL(nonfinite_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, p, bf16,
+                       rows, cols, ld, count);
+    return (int)hipGetLastError();
 }
 
 }  // namespace tsenor

@@ -37,8 +37,8 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings():
     l = sms.lib()
-    for s in range(7):
-        assert l.tsenor_status_str(s).decode()
+    for s in range(8):
+        assert l.tsenor_status_str(s).decode() != "unknown status"
     assert l.tsenor_status_str(99).decode() == "unknown status"
     assert sms.version() == 0x000100
 

@@ -471,3 +471,37 @@ def test_exact_cancel_limit():
     torch.cuda.synchronize()
     assert_feasible(words(m), rows, cols, N, M)
     assert np.isnan(objv.cpu().numpy()).any()
+
+
+def test_debug_checks_nonfinite(monkeypatch):
+    """TSENOR_DEBUG_CHECKS=1: a NaN or Inf anywhere in W (or S for the
+    rounding) is reported as status 7 before anything else runs; finite inputs
+    give the same masks as without the checks."""
+    import torch
+    M, N = 16, 8
+    W_np = _small(41, M, 9, 2, "student_t", True)
+    W = to_device(W_np)
+    ref, _ = sms.mask(W, N, M, 20.0, 30, 8)
+    monkeypatch.setenv("TSENOR_DEBUG_CHECKS", "1")
+    _note("debug checks, finite input")
+    got, _ = sms.mask(W, N, M, 20.0, 30, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    for val in (float("nan"), float("inf"), float("-inf")):
+        Wb = W.clone()
+        Wb[5, 77] = val
+        _note(f"debug checks, W holds {val}")
+        with pytest.raises(sms.TsenorError) as ei:
+            sms.mask(Wb, N, M, 20.0, 30, 8)
+        assert ei.value.status == 7
+        with pytest.raises(sms.TsenorError) as ei:
+            sms.mask_batched([(Wb, N, M)], 20.0, 30, 8)
+        assert ei.value.status == 7
+    S = torch.rand(W.shape, device="cuda")
+    S[3, 3] = float("nan")
+    with pytest.raises(sms.TsenorError) as ei:
+        sms.round_mask(S, W, N, M, 8)
+    assert ei.value.status == 7
+    monkeypatch.setenv("TSENOR_DEBUG_CHECKS", "0")
+    sms.mask(Wb, N, M, 20.0, 30, 8)  # unchecked: runs (result undefined)
+    torch.cuda.synchronize()
