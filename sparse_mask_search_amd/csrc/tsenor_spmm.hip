@@ -33,6 +33,7 @@ typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 // One thread per (row of A, 32-wide chunk of k): element (r, c) of A is
 // W[r][c] (trans = 0) or W[c][r] (trans = 1); mask bit likewise.  Groups with
@@ -155,6 +156,142 @@ __global__ __launch_bounds__(256) void spmm24_kernel(const uint16_t* __restrict_
         }
 }
 
+// The same product for m and n multiples of 64*WM and 64*WN and k of 64: a
+// workgroup of 2 x 2 waves owns a (64 WM) x (64 WN) tile of (m, n), a wave
+// WM x WN smfmac tiles, so each operand it reads feeds WN (A) or WM (B)
+// instructions.  Both operands are staged through LDS in k-steps of 64 with
+// coalesced global loads, double-buffered: the next step's loads are issued
+// before the current step's instructions and written to the other buffer
+// after them.  Swizzles keep the LDS reads conflict-free: row r of X keeps
+// its eight 16-byte chunks at c ^ ((r >> 1) & 7) (16 rows, one chunk per
+// pass), row r of A its eight 8-byte units at u ^ ((r >> 2) & 7) (32 rows,
+// one unit per pass).
+template <int WM, int WN>
+__global__ __launch_bounds__(256) void spmm24_tiled_kernel(const uint16_t* __restrict__ X,
+                                                           int64_t ldx,
+                                                           const uint16_t* __restrict__ vals,
+                                                           const uint32_t* __restrict__ meta,
+                                                           float* __restrict__ Y, int64_t ldy,
+                                                           int64_t m, int64_t k) {
+    constexpr int TM = 64 * WM, TN = 64 * WN;
+    constexpr int NX = TN * 8 / 256;  // 16-byte chunks of X per thread per k-step
+    constexpr int NA = TM * 4 / 256;  // 16-byte chunks of A values per thread per k-step
+    static_assert(TM <= 256, "one meta row per thread");
+    __shared__ u32x4 Xs[2][TN * 8];
+    __shared__ u32x2 As[2][TM * 8];
+    __shared__ u32x2 Ms[2][TM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int64_t tiles_m = m / TM;
+    const int64_t m0 = (blockIdx.x % tiles_m) * TM, n0 = (blockIdx.x / tiles_m) * TN;
+    const int64_t kh = k / 2, kw = k / 32;
+    const int steps = (int)(k / 64);
+
+    // global -> LDS copy assignments (fixed per thread)
+    const uint16_t* xsrc[NX];
+    int xdst[NX];
+#pragma unroll
+    for (int j = 0; j < NX; ++j) {
+        const int u = j * 256 + tid, row = u >> 3, c = u & 7;
+        xsrc[j] = X + (n0 + row) * ldx + 8 * c;
+        xdst[j] = row * 8 + (c ^ ((row >> 1) & 7));
+    }
+    const uint16_t* asrc[NA];
+    int adst0[NA], adst1[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+        const int u = j * 256 + tid, row = u >> 2, c = u & 3, f = (row >> 2) & 7;
+        asrc[j] = vals + (m0 + row) * kh + 8 * c;
+        adst0[j] = row * 8 + ((2 * c) ^ f);
+        adst1[j] = row * 8 + ((2 * c + 1) ^ f);
+    }
+    const bool has_meta = tid < TM;
+    const uint32_t* msrc = meta + (m0 + (has_meta ? tid : 0)) * kw;
+
+    u32x4 xreg[NX], areg[NA];
+    u32x2 mreg;
+    f32x16 acc[WM][WN];
+#pragma unroll
+    for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int b = 0; b < WN; ++b)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) acc[a][b][t] = 0.f;
+
+#define SPMM_LOAD(ST)                                                                        \
+    {                                                                                        \
+        _Pragma("unroll") for (int j = 0; j < NX; ++j)                                       \
+            xreg[j] = *reinterpret_cast<const u32x4*>(xsrc[j] + 64 * (ST));                   \
+        _Pragma("unroll") for (int j = 0; j < NA; ++j)                                       \
+            areg[j] = *reinterpret_cast<const u32x4*>(asrc[j] + 32 * (ST));                   \
+        if (has_meta) mreg = *reinterpret_cast<const u32x2*>(msrc + 2 * (ST));               \
+    }
+#define SPMM_STORE(BUF)                                                                      \
+    {                                                                                        \
+        _Pragma("unroll") for (int j = 0; j < NX; ++j) Xs[(BUF)][xdst[j]] = xreg[j];         \
+        _Pragma("unroll") for (int j = 0; j < NA; ++j) {                                     \
+            As[(BUF)][adst0[j]] = u32x2{areg[j].x, areg[j].y};                               \
+            As[(BUF)][adst1[j]] = u32x2{areg[j].z, areg[j].w};                               \
+        }                                                                                    \
+        if (has_meta) Ms[(BUF)][tid] = mreg;                                                 \
+    }
+    // one k-step from buffer BUF
+#define SPMM_STEP(ST, BUF)                                                                   \
+    {                                                                                        \
+        const bool more_ = (ST) + 1 < steps;                                                 \
+        if (more_) SPMM_LOAD((ST) + 1)                                                       \
+        _Pragma("unroll") for (int kc = 0; kc < 2; ++kc) {                                   \
+            bf16x16 bv[WN];                                                                  \
+            _Pragma("unroll") for (int b = 0; b < WN; ++b) {                                 \
+                const int row = 32 * (WN * wn + b) + l32, sw = (row >> 1) & 7;               \
+                const int c0 = 4 * kc + 2 * h;                                               \
+                const u32x4 p = Xs[(BUF)][row * 8 + (c0 ^ sw)];                              \
+                const u32x4 q = Xs[(BUF)][row * 8 + ((c0 + 1) ^ sw)];                        \
+                const u32x8 w8 = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};                   \
+                bv[b] = __builtin_bit_cast(bf16x16, w8);                                     \
+            }                                                                                \
+            _Pragma("unroll") for (int a = 0; a < WM; ++a) {                                 \
+                const int row = 32 * (WM * wm + a) + l32, f = (row >> 2) & 7;                \
+                const u32x2 lo = As[(BUF)][row * 8 + ((4 * kc + h) ^ f)];                    \
+                const u32x2 hi = As[(BUF)][row * 8 + ((4 * kc + 2 + h) ^ f)];                \
+                const u32x4 w4 = {lo.x, lo.y, hi.x, hi.y};                                   \
+                const bf16x8 aval = __builtin_bit_cast(bf16x8, w4);                          \
+                const u32x2 mm = Ms[(BUF)][row];                                             \
+                const uint32_t mw = kc ? mm.y : mm.x;                                        \
+                const int idx =                                                              \
+                    (int)(((mw >> (8 * h)) & 0xFFu) | (((mw >> (16 + 8 * h)) & 0xFFu) << 8)); \
+                _Pragma("unroll") for (int b = 0; b < WN; ++b) acc[a][b] =                   \
+                    __builtin_amdgcn_smfmac_f32_32x32x32_bf16(aval, bv[b], acc[a][b], idx, 0, 0); \
+            }                                                                                \
+        }                                                                                    \
+        if (more_) SPMM_STORE((BUF) ^ 1)                                                     \
+        __syncthreads();                                                                     \
+    }
+
+    SPMM_LOAD(0)
+    SPMM_STORE(0)
+    __syncthreads();
+    for (int st = 0; st < steps; st += 2) {
+        SPMM_STEP(st, 0)
+        if (st + 1 < steps) SPMM_STEP(st + 1, 1)
+    }
+#undef SPMM_STEP
+#undef SPMM_STORE
+#undef SPMM_LOAD
+#pragma unroll
+    for (int a = 0; a < WM; ++a)
+#pragma unroll
+        for (int b = 0; b < WN; ++b) {
+            float* y = Y + (n0 + 32 * (WN * wn + b) + l32) * ldy + m0 + 32 * (WM * wm + a) + 4 * h;
+#pragma unroll
+            for (int i0 = 0; i0 < 4; ++i0)
+                *reinterpret_cast<float4*>(y + 8 * i0) =
+                    make_float4(acc[a][b][4 * i0], acc[a][b][4 * i0 + 1], acc[a][b][4 * i0 + 2],
+                                acc[a][b][4 * i0 + 3]);
+        }
+}
+
 }  // namespace
 
 int launch_compress24(const uint16_t* W, int64_t ld, const uint32_t* mask, int64_t wpr,
@@ -169,6 +306,15 @@ int launch_compress24(const uint16_t* W, int64_t ld, const uint32_t* mask, int64
 
 int launch_spmm24(const uint16_t* X, int64_t ldx, const uint16_t* vals, const uint32_t* meta,
                   float* Y, int64_t ldy, int64_t n, int64_t m, int64_t k, void* stream) {
+    constexpr int WM = 4, WN = 4;
+    if (m % (64 * WM) == 0 && n % (64 * WN) == 0 && k % 64 == 0 && ldx % 8 == 0 &&
+        (reinterpret_cast<uintptr_t>(meta) & 7u) == 0 &&
+        (reinterpret_cast<uintptr_t>(vals) & 15u) == 0) {
+        const int64_t blocks = (m / (64 * WM)) * (n / (64 * WN));
+        hipLaunchKernelGGL((spmm24_tiled_kernel<WM, WN>), dim3((unsigned)blocks), dim3(256), 0,
+                           (hipStream_t)stream, X, ldx, vals, meta, Y, ldy, m, k);
+        return (int)hipGetLastError();
+    }
     const int64_t blocks = (m / 128) * (n / 128);
     hipLaunchKernelGGL(spmm24_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, X,
                        ldx, vals, meta, Y, ldy, n, m, k);

@@ -52,7 +52,7 @@ def test_overfull_groups_counted_on_gpu():
     assert np.array_equal(meta.cpu().numpy().view(np.uint32), m0)
 
 
-@pytest.mark.parametrize("n,rows,cols", [(128, 256, 384), (256, 512, 256)])
+@pytest.mark.parametrize("n,rows,cols", [(128, 256, 384), (256, 512, 256), (512, 768, 1408)])
 def test_forward_and_data_gradient(n, rows, cols):
     import torch
     print(f"[case] spmm n={n} W {rows}x{cols}", flush=True)
@@ -73,3 +73,22 @@ def test_forward_and_data_gradient(n, rows, cols):
                             (dX, Gd @ Wd, np.abs(Gd) @ np.abs(Wd))):
         err = np.abs(got.cpu().numpy() - ref)
         assert (err <= 1e-5 * bound + 1e-30).all(), err.max()
+
+
+def test_forward_odd_k_steps():
+    """k = 320: an odd number of 64-wide k-steps (the staged kernel's last
+    step has no successor to prefetch); m, n multiples of 256."""
+    import torch
+    n, rows, cols = 256, 512, 320
+    print(f"[case] spmm odd k-steps n={n} W {rows}x{cols}", flush=True)
+    Wb, W, m = _case(11, rows, cols)
+    rng = np.random.default_rng(12)
+    Z = oracle.unpack_mask(words(m), cols)
+    Wd = wl.bf16_bits_to_f32(Wb).astype(np.float64) * Z
+    Xb = wl.f32_to_bf16_bits(rng.standard_normal((n, cols)).astype(np.float32))
+    Xd = wl.bf16_bits_to_f32(Xb).astype(np.float64)
+    vf, mf, _ = sms.compress24(W, m)
+    Y = sms.spmm24(to_device(Xb), vf, mf)
+    torch.cuda.synchronize()
+    err = np.abs(Y.cpu().numpy() - Xd @ Wd.T)
+    assert (err <= 1e-5 * (np.abs(Xd) @ np.abs(Wd).T) + 1e-30).all(), err.max()
