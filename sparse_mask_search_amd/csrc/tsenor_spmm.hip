@@ -156,32 +156,33 @@ __global__ __launch_bounds__(256) void spmm24_kernel(const uint16_t* __restrict_
         }
 }
 
-// The same product for m and n multiples of 64*WM and 64*WN and k of 64: a
-// workgroup of 2 x 2 waves owns a (64 WM) x (64 WN) tile of (m, n), a wave
-// WM x WN smfmac tiles, so each operand it reads feeds WN (A) or WM (B)
-// instructions.  Both operands are staged through LDS in k-steps of 64 with
+// The same product for m and n multiples of the workgroup tile and k of 64:
+// a workgroup of GM x GN waves owns a (32 WM GM) x (32 WN GN) tile of (m, n),
+// a wave WM x WN smfmac tiles, so each operand it reads feeds WN (A) or WM
+// (B) instructions.  Both operands are staged through LDS in k-steps of 64 with
 // coalesced global loads, double-buffered: the next step's loads are issued
 // before the current step's instructions and written to the other buffer
 // after them.  Swizzles keep the LDS reads conflict-free: row r of X keeps
 // its eight 16-byte chunks at c ^ ((r >> 1) & 7) (16 rows, one chunk per
 // pass), row r of A its eight 8-byte units at u ^ ((r >> 2) & 7) (32 rows,
 // one unit per pass).
-template <int WM, int WN>
-__global__ __launch_bounds__(256) void spmm24_tiled_kernel(const uint16_t* __restrict__ X,
+template <int WM, int WN, int GM, int GN>
+__global__ __launch_bounds__(64 * GM * GN) void spmm24_tiled_kernel(const uint16_t* __restrict__ X,
                                                            int64_t ldx,
                                                            const uint16_t* __restrict__ vals,
                                                            const uint32_t* __restrict__ meta,
                                                            float* __restrict__ Y, int64_t ldy,
                                                            int64_t m, int64_t k) {
-    constexpr int TM = 64 * WM, TN = 64 * WN;
-    constexpr int NX = TN * 8 / 256;  // 16-byte chunks of X per thread per k-step
-    constexpr int NA = TM * 4 / 256;  // 16-byte chunks of A values per thread per k-step
-    static_assert(TM <= 256, "one meta row per thread");
+    constexpr int NT = 64 * GM * GN;      // threads
+    constexpr int TM = 32 * WM * GM, TN = 32 * WN * GN;
+    constexpr int NX = TN * 8 / NT;  // 16-byte chunks of X per thread per k-step
+    constexpr int NA = TM * 4 / NT;  // 16-byte chunks of A values per thread per k-step
+    static_assert(TM <= NT && NX * NT == TN * 8 && NA * NT == TM * 4, "copy assignment");
     __shared__ u32x4 Xs[2][TN * 8];
     __shared__ u32x2 As[2][TM * 8];
     __shared__ u32x2 Ms[2][TM];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / GN, wn = wave % GN;
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t tiles_m = m / TM;
     const int64_t m0 = (blockIdx.x % tiles_m) * TM, n0 = (blockIdx.x / tiles_m) * TN;
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(256) void spmm24_tiled_kernel(const uint16_t* __res
     int xdst[NX];
 #pragma unroll
     for (int j = 0; j < NX; ++j) {
-        const int u = j * 256 + tid, row = u >> 3, c = u & 7;
+        const int u = j * NT + tid, row = u >> 3, c = u & 7;
         xsrc[j] = X + (n0 + row) * ldx + 8 * c;
         xdst[j] = row * 8 + (c ^ ((row >> 1) & 7));
     }
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(256) void spmm24_tiled_kernel(const uint16_t* __res
     int adst0[NA], adst1[NA];
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
-        const int u = j * 256 + tid, row = u >> 2, c = u & 3, f = (row >> 2) & 7;
+        const int u = j * NT + tid, row = u >> 2, c = u & 3, f = (row >> 2) & 7;
         asrc[j] = vals + (m0 + row) * kh + 8 * c;
         adst0[j] = row * 8 + ((2 * c) ^ f);
         adst1[j] = row * 8 + ((2 * c + 1) ^ f);
@@ -236,33 +237,43 @@ __global__ __launch_bounds__(256) void spmm24_tiled_kernel(const uint16_t* __res
         }                                                                                    \
         if (has_meta) Ms[(BUF)][tid] = mreg;                                                 \
     }
-    // one k-step from buffer BUF
+    // One k-step from LDS buffer BUF: every operand of the step is read first
+    // (a single LDS latency per step; the first half's instructions start as
+    // soon as their operands are in), then the 2 WM WN instructions.
 #define SPMM_STEP(ST, BUF)                                                                   \
     {                                                                                        \
         const bool more_ = (ST) + 1 < steps;                                                 \
         if (more_) SPMM_LOAD((ST) + 1)                                                       \
+        bf16x16 bv[2][WN];                                                                   \
+        bf16x8 avv[2][WM];                                                                   \
+        u32x2 mmv[WM];                                                                       \
         _Pragma("unroll") for (int kc = 0; kc < 2; ++kc) {                                   \
-            bf16x16 bv[WN];                                                                  \
             _Pragma("unroll") for (int b = 0; b < WN; ++b) {                                 \
                 const int row = 32 * (WN * wn + b) + l32, sw = (row >> 1) & 7;               \
                 const int c0 = 4 * kc + 2 * h;                                               \
                 const u32x4 p = Xs[(BUF)][row * 8 + (c0 ^ sw)];                              \
                 const u32x4 q = Xs[(BUF)][row * 8 + ((c0 + 1) ^ sw)];                        \
                 const u32x8 w8 = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};                   \
-                bv[b] = __builtin_bit_cast(bf16x16, w8);                                     \
+                bv[kc][b] = __builtin_bit_cast(bf16x16, w8);                                 \
             }                                                                                \
             _Pragma("unroll") for (int a = 0; a < WM; ++a) {                                 \
                 const int row = 32 * (WM * wm + a) + l32, f = (row >> 2) & 7;                \
                 const u32x2 lo = As[(BUF)][row * 8 + ((4 * kc + h) ^ f)];                    \
                 const u32x2 hi = As[(BUF)][row * 8 + ((4 * kc + 2 + h) ^ f)];                \
                 const u32x4 w4 = {lo.x, lo.y, hi.x, hi.y};                                   \
-                const bf16x8 aval = __builtin_bit_cast(bf16x8, w4);                          \
-                const u32x2 mm = Ms[(BUF)][row];                                             \
-                const uint32_t mw = kc ? mm.y : mm.x;                                        \
+                avv[kc][a] = __builtin_bit_cast(bf16x8, w4);                                 \
+                if (kc == 0) mmv[a] = Ms[(BUF)][row];                                        \
+            }                                                                                \
+        }                                                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        _Pragma("unroll") for (int kc = 0; kc < 2; ++kc) {                                   \
+            _Pragma("unroll") for (int a = 0; a < WM; ++a) {                                 \
+                const uint32_t mw = kc ? mmv[a].y : mmv[a].x;                                \
                 const int idx =                                                              \
                     (int)(((mw >> (8 * h)) & 0xFFu) | (((mw >> (16 + 8 * h)) & 0xFFu) << 8)); \
                 _Pragma("unroll") for (int b = 0; b < WN; ++b) acc[a][b] =                   \
-                    __builtin_amdgcn_smfmac_f32_32x32x32_bf16(aval, bv[b], acc[a][b], idx, 0, 0); \
+                    __builtin_amdgcn_smfmac_f32_32x32x32_bf16(avv[kc][a], bv[kc][b], acc[a][b], \
+                                                              idx, 0, 0);                    \
             }                                                                                \
         }                                                                                    \
         if (more_) SPMM_STORE((BUF) ^ 1)                                                     \
@@ -306,13 +317,15 @@ int launch_compress24(const uint16_t* W, int64_t ld, const uint32_t* mask, int64
 
 int launch_spmm24(const uint16_t* X, int64_t ldx, const uint16_t* vals, const uint32_t* meta,
                   float* Y, int64_t ldy, int64_t n, int64_t m, int64_t k, void* stream) {
-    constexpr int WM = 4, WN = 4;
-    if (m % (64 * WM) == 0 && n % (64 * WN) == 0 && k % 64 == 0 && ldx % 8 == 0 &&
+    constexpr int WM = 4, WN = 4, GM = 2, GN = 2;
+    constexpr int TM = 32 * WM * GM, TN = 32 * WN * GN;
+    if (m % TM == 0 && n % TN == 0 && k % 64 == 0 && ldx % 8 == 0 &&
         (reinterpret_cast<uintptr_t>(meta) & 7u) == 0 &&
         (reinterpret_cast<uintptr_t>(vals) & 15u) == 0) {
-        const int64_t blocks = (m / (64 * WM)) * (n / (64 * WN));
-        hipLaunchKernelGGL((spmm24_tiled_kernel<WM, WN>), dim3((unsigned)blocks), dim3(256), 0,
-                           (hipStream_t)stream, X, ldx, vals, meta, Y, ldy, m, k);
+        const int64_t blocks = (m / TM) * (n / TN);
+        hipLaunchKernelGGL((spmm24_tiled_kernel<WM, WN, GM, GN>), dim3((unsigned)blocks),
+                           dim3(64 * GM * GN), 0, (hipStream_t)stream, X, ldx, vals, meta, Y, ldy,
+                           m, k);
         return (int)hipGetLastError();
     }
     const int64_t blocks = (m / 128) * (n / 128);
