@@ -156,62 +156,82 @@ __global__ __launch_bounds__(256) void spmm24_kernel(const uint16_t* __restrict_
         }
 }
 
-// The same product for m and n multiples of the workgroup tile and k of 64:
-// a workgroup of GM x GN waves owns a (32 WM GM) x (32 WN GN) tile of (m, n),
-// a wave WM x WN smfmac tiles, so each operand it reads feeds WN (A) or WM
-// (B) instructions.  Both operands are staged through LDS in k-steps of 64 with
-// coalesced global loads, double-buffered: the next step's loads are issued
-// before the current step's instructions and written to the other buffer
-// after them.  Swizzles keep the LDS reads conflict-free: row r of X keeps
-// its eight 16-byte chunks at c ^ ((r >> 1) & 7) (16 rows, one chunk per
-// pass), row r of A its eight 8-byte units at u ^ ((r >> 2) & 7) (32 rows,
-// one unit per pass).
-template <int WM, int WN, int GM, int GN>
-__global__ __launch_bounds__(64 * GM * GN) void spmm24_tiled_kernel(const uint16_t* __restrict__ X,
-                                                           int64_t ldx,
-                                                           const uint16_t* __restrict__ vals,
-                                                           const uint32_t* __restrict__ meta,
-                                                           float* __restrict__ Y, int64_t ldy,
-                                                           int64_t m, int64_t k) {
-    constexpr int NT = 64 * GM * GN;      // threads
-    constexpr int TM = 32 * WM * GM, TN = 32 * WN * GN;
-    constexpr int NX = TN * 8 / NT;  // 16-byte chunks of X per thread per k-step
-    constexpr int NA = TM * 4 / NT;  // 16-byte chunks of A values per thread per k-step
-    static_assert(TM <= NT && NX * NT == TN * 8 && NA * NT == TM * 4, "copy assignment");
-    __shared__ u32x4 Xs[2][TN * 8];
-    __shared__ u32x2 As[2][TM * 8];
-    __shared__ u32x2 Ms[2][TM];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / GN, wn = wave % GN;
+// The same product for m and n multiples of 64 WM and 64 WN and k of 64: a
+// workgroup of 2 x 2 waves owns a (64 WM) x (64 WN) tile of (m, n), a wave
+// WM x WN smfmac tiles (accumulators in AGPRs, one wave per SIMD), so each
+// operand read from LDS feeds WN (A) or WM (B) instructions.  Both operands
+// reach LDS by direct loads (global_load_lds_dwordx4: lane l's 16 bytes land
+// at the instruction's LDS base + 16 l), with no register staging, into a
+// ring of three k-step buffers filled two steps ahead.  Swizzles keep the LDS
+// reads conflict-free for X (row r keeps its eight 16-byte chunks at
+// c ^ ((r >> 1) & 7): the 16 rows of one pass hit 16 bank groups) and at most
+// two-way for A (row r keeps its four 16-byte chunks at c ^ ((r >> 2) & 3)).
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One lane's 16 (or 4) bytes from global memory to LDS at base + 16 l (4 l).
+// Written in asm because the compiler cannot tell the ring buffers apart: it
+// would wait for every outstanding direct load before each LDS read, which
+// serialises the ring.  The kernel waits for them itself (vmcnt) before the
+// barrier that publishes a buffer.  No register receives data, so nothing is
+// left in flight in a VGPR.  M0 carries the LDS base; nothing else in this
+// kernel uses M0 (checked in its ISA), and the clobber tells the compiler.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is a reserved register; see above
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(g), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int WM, int WN>
+__global__ __launch_bounds__(256) void spmm24_dma_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                         const uint16_t* __restrict__ vals,
+                                                         const uint32_t* __restrict__ meta,
+                                                         float* __restrict__ Y, int64_t ldy,
+                                                         int64_t m, int64_t k) {
+    constexpr int TM = 64 * WM, TN = 64 * WN;
+    static_assert(TN % 32 == 0 && TM % 64 == 0, "tile");
+    constexpr int QX = TN / 8 / 4;   // 1 KiB X instructions per wave per step (8 rows each)
+    constexpr int QA = TM / 16 / 4;  // 1 KiB A instructions per wave (16 rows each)
+    constexpr int QM = TM / 32 / 4;  // 256 B position instructions per wave (32 rows each)
+    __shared__ u32x4 Xs0[TN * 8], Xs1[TN * 8], Xs2[TN * 8];
+    __shared__ u32x2 As0[TM * 8], As1[TM * 8], As2[TM * 8];
+    __shared__ u32x2 Ms0[TM], Ms1[TM], Ms2[TM];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
     const int64_t tiles_m = m / TM;
     const int64_t m0 = (blockIdx.x % tiles_m) * TM, n0 = (blockIdx.x / tiles_m) * TN;
     const int64_t kh = k / 2, kw = k / 32;
     const int steps = (int)(k / 64);
 
-    // global -> LDS copy assignments (fixed per thread)
-    const uint16_t* xsrc[NX];
-    int xdst[NX];
+    // per-lane global sources of this wave's instructions (step 0)
+    const uint16_t* xsrc[QX];
 #pragma unroll
-    for (int j = 0; j < NX; ++j) {
-        const int u = j * NT + tid, row = u >> 3, c = u & 7;
-        xsrc[j] = X + (n0 + row) * ldx + 8 * c;
-        xdst[j] = row * 8 + (c ^ ((row >> 1) & 7));
+    for (int j = 0; j < QX; ++j) {
+        const int q = wave * QX + j, row = 8 * q + (lane >> 3), p = lane & 7;
+        xsrc[j] = X + (n0 + row) * ldx + 8 * (p ^ ((row >> 1) & 7));
     }
-    const uint16_t* asrc[NA];
-    int adst0[NA], adst1[NA];
+    const uint16_t* asrc[QA];
 #pragma unroll
-    for (int j = 0; j < NA; ++j) {
-        const int u = j * NT + tid, row = u >> 2, c = u & 3, f = (row >> 2) & 7;
-        asrc[j] = vals + (m0 + row) * kh + 8 * c;
-        adst0[j] = row * 8 + ((2 * c) ^ f);
-        adst1[j] = row * 8 + ((2 * c + 1) ^ f);
+    for (int j = 0; j < QA; ++j) {
+        const int q = wave * QA + j, row = 16 * q + (lane >> 2), sl = lane & 3;
+        asrc[j] = vals + (m0 + row) * kh + 8 * (sl ^ ((row >> 2) & 3));
     }
-    const bool has_meta = tid < TM;
-    const uint32_t* msrc = meta + (m0 + (has_meta ? tid : 0)) * kw;
-
-    u32x4 xreg[NX], areg[NA];
-    u32x2 mreg;
+    const uint32_t* msrc[QM];
+#pragma unroll
+    for (int j = 0; j < QM; ++j) {
+        const int q = wave * QM + j, row = 32 * q + (lane >> 1);
+        msrc[j] = meta + (m0 + row) * kw + (lane & 1);
+    }
     f32x16 acc[WM][WN];
 #pragma unroll
     for (int a = 0; a < WM; ++a)
@@ -220,30 +240,20 @@ __global__ __launch_bounds__(64 * GM * GN) void spmm24_tiled_kernel(const uint16
 #pragma unroll
             for (int t = 0; t < 16; ++t) acc[a][b][t] = 0.f;
 
-#define SPMM_LOAD(ST)                                                                        \
+    // issue the loads of k-step ST (clamped to the last step: a repeated
+    // step lands in a buffer no later step reads) into buffer set XB/AB/MB
+#define SPMM_ISSUE(ST, XB, AB, MB)                                                           \
     {                                                                                        \
-        _Pragma("unroll") for (int j = 0; j < NX; ++j)                                       \
-            xreg[j] = *reinterpret_cast<const u32x4*>(xsrc[j] + 64 * (ST));                   \
-        _Pragma("unroll") for (int j = 0; j < NA; ++j)                                       \
-            areg[j] = *reinterpret_cast<const u32x4*>(asrc[j] + 32 * (ST));                   \
-        if (has_meta) mreg = *reinterpret_cast<const u32x2*>(msrc + 2 * (ST));               \
+        const int s_ = (ST) < steps ? (ST) : steps - 1;                                      \
+        _Pragma("unroll") for (int j = 0; j < QX; ++j)                                       \
+            dma16(xsrc[j] + 64 * s_, lds_offset((XB) + (wave * QX + j) * 64));                 \
+        _Pragma("unroll") for (int j = 0; j < QA; ++j)                                       \
+            dma16(asrc[j] + 32 * s_, lds_offset((AB) + (wave * QA + j) * 128));                \
+        _Pragma("unroll") for (int j = 0; j < QM; ++j)                                       \
+            dma4(msrc[j] + 2 * s_, lds_offset((MB) + (wave * QM + j) * 32));                   \
     }
-#define SPMM_STORE(BUF)                                                                      \
+#define SPMM_COMPUTE(XB, AB, MB)                                                             \
     {                                                                                        \
-        _Pragma("unroll") for (int j = 0; j < NX; ++j) Xs[(BUF)][xdst[j]] = xreg[j];         \
-        _Pragma("unroll") for (int j = 0; j < NA; ++j) {                                     \
-            As[(BUF)][adst0[j]] = u32x2{areg[j].x, areg[j].y};                               \
-            As[(BUF)][adst1[j]] = u32x2{areg[j].z, areg[j].w};                               \
-        }                                                                                    \
-        if (has_meta) Ms[(BUF)][tid] = mreg;                                                 \
-    }
-    // One k-step from LDS buffer BUF: every operand of the step is read first
-    // (a single LDS latency per step; the first half's instructions start as
-    // soon as their operands are in), then the 2 WM WN instructions.
-#define SPMM_STEP(ST, BUF)                                                                   \
-    {                                                                                        \
-        const bool more_ = (ST) + 1 < steps;                                                 \
-        if (more_) SPMM_LOAD((ST) + 1)                                                       \
         bf16x16 bv[2][WN];                                                                   \
         bf16x8 avv[2][WM];                                                                   \
         u32x2 mmv[WM];                                                                       \
@@ -251,18 +261,18 @@ __global__ __launch_bounds__(64 * GM * GN) void spmm24_tiled_kernel(const uint16
             _Pragma("unroll") for (int b = 0; b < WN; ++b) {                                 \
                 const int row = 32 * (WN * wn + b) + l32, sw = (row >> 1) & 7;               \
                 const int c0 = 4 * kc + 2 * h;                                               \
-                const u32x4 p = Xs[(BUF)][row * 8 + (c0 ^ sw)];                              \
-                const u32x4 q = Xs[(BUF)][row * 8 + ((c0 + 1) ^ sw)];                        \
+                const u32x4 p = (XB)[row * 8 + (c0 ^ sw)];                                   \
+                const u32x4 q = (XB)[row * 8 + ((c0 + 1) ^ sw)];                             \
                 const u32x8 w8 = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};                   \
                 bv[kc][b] = __builtin_bit_cast(bf16x16, w8);                                 \
             }                                                                                \
             _Pragma("unroll") for (int a = 0; a < WM; ++a) {                                 \
-                const int row = 32 * (WM * wm + a) + l32, f = (row >> 2) & 7;                \
-                const u32x2 lo = As[(BUF)][row * 8 + ((4 * kc + h) ^ f)];                    \
-                const u32x2 hi = As[(BUF)][row * 8 + ((4 * kc + 2 + h) ^ f)];                \
+                const int row = 32 * (WM * wm + a) + l32, g = (row >> 2) & 3;                \
+                const u32x2 lo = (AB)[row * 8 + 2 * ((2 * kc) ^ g) + h];                     \
+                const u32x2 hi = (AB)[row * 8 + 2 * ((2 * kc + 1) ^ g) + h];                 \
                 const u32x4 w4 = {lo.x, lo.y, hi.x, hi.y};                                   \
                 avv[kc][a] = __builtin_bit_cast(bf16x8, w4);                                 \
-                if (kc == 0) mmv[a] = Ms[(BUF)][row];                                        \
+                if (kc == 0) mmv[a] = (MB)[row];                                             \
             }                                                                                \
         }                                                                                    \
         __builtin_amdgcn_sched_barrier(0);                                                   \
@@ -276,20 +286,35 @@ __global__ __launch_bounds__(64 * GM * GN) void spmm24_tiled_kernel(const uint16
                                                               idx, 0, 0);                    \
             }                                                                                \
         }                                                                                    \
-        if (more_) SPMM_STORE((BUF) ^ 1)                                                     \
-        __syncthreads();                                                                     \
+    }
+    // k-step ST from buffer set 0/1/2: its loads are complete once at most the
+    // next step's are outstanding, and every LDS read of the previous step is
+    // done; after the barrier every wave's part is visible and the buffer the
+    // step after next fills is no longer read by anyone.
+#define SPMM_DSTEP(ST, XB, AB, MB, XN, AN, MN)                                               \
+    {                                                                                        \
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(QX + QA + QM) : "memory");      \
+        __builtin_amdgcn_s_barrier();                                                        \
+        asm volatile("" ::: "memory");                                                       \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        SPMM_ISSUE((ST) + 2, XN, AN, MN)                                                     \
+        SPMM_COMPUTE(XB, AB, MB)                                                             \
     }
 
-    SPMM_LOAD(0)
-    SPMM_STORE(0)
-    __syncthreads();
-    for (int st = 0; st < steps; st += 2) {
-        SPMM_STEP(st, 0)
-        if (st + 1 < steps) SPMM_STEP(st + 1, 1)
+    SPMM_ISSUE(0, Xs0, As0, Ms0)
+    SPMM_ISSUE(1, Xs1, As1, Ms1)
+    int st = 0;
+    for (; st + 3 <= steps; st += 3) {
+        SPMM_DSTEP(st, Xs0, As0, Ms0, Xs2, As2, Ms2)
+        SPMM_DSTEP(st + 1, Xs1, As1, Ms1, Xs0, As0, Ms0)
+        SPMM_DSTEP(st + 2, Xs2, As2, Ms2, Xs1, As1, Ms1)
     }
-#undef SPMM_STEP
-#undef SPMM_STORE
-#undef SPMM_LOAD
+    if (st < steps) SPMM_DSTEP(st, Xs0, As0, Ms0, Xs2, As2, Ms2)
+    if (st + 1 < steps) SPMM_DSTEP(st + 1, Xs1, As1, Ms1, Xs0, As0, Ms0)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef SPMM_DSTEP
+#undef SPMM_COMPUTE
+#undef SPMM_ISSUE
 #pragma unroll
     for (int a = 0; a < WM; ++a)
 #pragma unroll
@@ -317,15 +342,14 @@ int launch_compress24(const uint16_t* W, int64_t ld, const uint32_t* mask, int64
 
 int launch_spmm24(const uint16_t* X, int64_t ldx, const uint16_t* vals, const uint32_t* meta,
                   float* Y, int64_t ldy, int64_t n, int64_t m, int64_t k, void* stream) {
-    constexpr int WM = 4, WN = 4, GM = 2, GN = 2;
-    constexpr int TM = 32 * WM * GM, TN = 32 * WN * GN;
+    constexpr int WM = 4, WN = 4;
+    constexpr int TM = 64 * WM, TN = 64 * WN;
     if (m % TM == 0 && n % TN == 0 && k % 64 == 0 && ldx % 8 == 0 &&
         (reinterpret_cast<uintptr_t>(meta) & 7u) == 0 &&
         (reinterpret_cast<uintptr_t>(vals) & 15u) == 0) {
         const int64_t blocks = (m / TM) * (n / TN);
-        hipLaunchKernelGGL((spmm24_tiled_kernel<WM, WN, GM, GN>), dim3((unsigned)blocks),
-                           dim3(64 * GM * GN), 0, (hipStream_t)stream, X, ldx, vals, meta, Y, ldy,
-                           m, k);
+        hipLaunchKernelGGL((spmm24_dma_kernel<WM, WN>), dim3((unsigned)blocks), dim3(256), 0,
+                           (hipStream_t)stream, X, ldx, vals, meta, Y, ldy, m, k);
         return (int)hipGetLastError();
     }
     const int64_t blocks = (m / 128) * (n / 128);
