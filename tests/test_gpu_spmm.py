@@ -75,13 +75,15 @@ def test_forward_and_data_gradient(n, rows, cols):
         assert (err <= 1e-5 * bound + 1e-30).all(), err.max()
 
 
-def test_forward_odd_k_steps():
-    """k = 320: an odd number of 64-wide k-steps (the staged kernel's last
-    step has no successor to prefetch); m, n multiples of 256."""
+@pytest.mark.parametrize("cols", [64, 128, 192, 320, 384])
+def test_forward_k_step_counts(cols):
+    """m, n multiples of 256 (the LDS-ring kernel) with 1, 2, 3, 5 and 6
+    k-steps of 64: every position of the three-buffer ring at the end of the
+    loop, and rings shorter than the prefetch distance."""
     import torch
-    n, rows, cols = 256, 512, 320
-    print(f"[case] spmm odd k-steps n={n} W {rows}x{cols}", flush=True)
-    Wb, W, m = _case(11, rows, cols)
+    n, rows = 256, 512
+    print(f"[case] spmm k-steps n={n} W {rows}x{cols}", flush=True)
+    Wb, W, m = _case(11 + cols, rows, cols)
     rng = np.random.default_rng(12)
     Z = oracle.unpack_mask(words(m), cols)
     Wd = wl.bf16_bits_to_f32(Wb).astype(np.float64) * Z
