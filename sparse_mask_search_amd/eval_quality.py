@@ -68,7 +68,8 @@ def main(argv=None):
         rec = {"workload": args.workload, "polish_steps": K, "method_ms": round(t_m * 1e3, 3),
                "exact_from_method_ms": round(t_x * 1e3, 1),
                "blocks": int(opt.numel()), "uncertified_blocks": int((~ok).sum()),
-               "gap_mean": float(gap.mean()), "gap_max": float(gap.max()),
+               "gap_mean": float(gap.mean()), "gap_median": float(gap.median()),
+               "gap_p99": float(torch.quantile(gap.float(), 0.99)), "gap_max": float(gap.max()),
                "blocks_optimal": float((gap <= 1e-12).double().mean())}
         if t_exact is not None:
             rec["exact_from_circulant_ms"] = round(t_exact * 1e3, 1)

@@ -150,6 +150,25 @@ def test_other_n(M, N):
     assert_feasible(mask, rows, cols, N, M)
 
 
+@pytest.mark.parametrize("k", [-20, 9])
+@pytest.mark.parametrize("M,bf16", [(8, False), (32, True)])
+def test_power_of_two_scale_invariance(M, bf16, k):
+    """W and W * 2^k: the block-max normalisation removes the factor exactly
+    and the local-search scores scale exactly, so S and the mask are
+    bit-identical (the oracle's own pin of the method, here on the GPU)."""
+    import torch
+    N = M // 2
+    W_np = _small(600 + M, M, 13, 2, "student_t", False).astype(np.float32)
+    W2_np = np.ldexp(W_np, k).astype(np.float32)
+    if bf16:
+        W_np, W2_np = wl.f32_to_bf16_bits(W_np), wl.f32_to_bf16_bits(W2_np)
+    _note(f"scale 2^{k} M={M} bf16={bf16}")
+    _, m1, S1, _ = _run(W_np, N, M, 30.0, 60, M)
+    _, m2, S2, _ = _run(W2_np, N, M, 30.0, 60, M)
+    assert np.array_equal(m1, m2)
+    assert np.array_equal(S1, S2)
+
+
 @pytest.mark.parametrize("M", [4, 8, 16, 32])
 def test_closed_forms(M):
     """tau = 0: S = N/M everywhere and the mask is the block diagonal of N x N
