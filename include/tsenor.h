@@ -45,7 +45,7 @@
  *     S on every run and for every stream.  Non-finite weights give undefined
  *     (but memory-safe) results.
  *   - Debug checks: with the environment variable TSENOR_DEBUG_CHECKS=1 (read
- *     at every call), tsenor_mask, tsenor_mask_ex, tsenor_mask_batched,
+ *     at every call), tsenor_mask, tsenor_mask_ex, tsenor_mask_batched(_ex),
  *     tsenor_round and tsenor_exact first count the non-finite elements of
  *     their W (and S) on the device, wait for the count, and return
  *     TSENOR_ERR_NONFINITE without launching anything else if it is not zero.
@@ -179,15 +179,25 @@ typedef struct {
     float* frac_out; /* NULL = don't write */
 } tsenor_matrix;
 
-/* Many matrices (possibly of different shape, dtype and N:M) in one kernel
- * launch, e.g. every projection of a transformer.  `mats` is a HOST array of
- * `count` descriptors (count >= 0; 0 is a no-op); every descriptor is
- * validated as in tsenor_mask before anything is enqueued.  tau, iters and
- * ls_steps apply to all matrices.  The descriptor table is copied to the
- * device on `stream` before the call returns, so `mats` may be reused
- * immediately.                                                               */
+/* Many matrices (possibly of different shape, dtype and N:M) in one call, one
+ * kernel launch per (M, dtype) class present, e.g. every projection of a
+ * transformer.  `mats` is a HOST array of `count` descriptors (count >= 0; 0
+ * is a no-op); every descriptor is validated as in tsenor_mask before
+ * anything is enqueued.  tau, iters and ls_steps apply to all matrices.  The
+ * descriptor table is copied to the device on `stream` before the call
+ * returns, so `mats` may be reused immediately.  Each matrix's mask and S
+ * are those tsenor_mask gives for it alone.                                  */
 int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int iters,
                         int ls_steps, void* stream);
+
+/* tsenor_mask_batched with tsenor_mask_ex's optional stages for every matrix:
+ * polish_steps >= 0 as in tsenor_mask_ex; prev_masks is NULL or a HOST array
+ * of `count` device pointers, entry i a previous mask for matrix i (layout of
+ * its mask_out; may alias that mask_out) or NULL.  Each matrix's result equals
+ * tsenor_mask_ex's for it alone.  polish_steps < 0 is TSENOR_ERR_PARAM.       */
+int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int iters,
+                           int ls_steps, int polish_steps, const uint32_t* const* prev_masks,
+                           void* stream);
 
 /* Rounding only (step 3) on a caller-supplied fractional matrix S.
  *   S        device, [rows][lds] fp32, values in [0, 1] (as produced by the

@@ -59,6 +59,9 @@ def lib():
         l.tsenor_round.restype = _I
         l.tsenor_mask_batched.argtypes = [ctypes.POINTER(_Matrix), _I, _F, _I, _I, _P]
         l.tsenor_mask_batched.restype = _I
+        l.tsenor_mask_batched_ex.argtypes = [ctypes.POINTER(_Matrix), _I, _F, _I, _I, _I,
+                                             ctypes.POINTER(_P), _P]
+        l.tsenor_mask_batched_ex.restype = _I
         l.tsenor_status_str.argtypes = [_I]
         l.tsenor_status_str.restype = ctypes.c_char_p
         l.tsenor_last_error.argtypes = []
@@ -243,15 +246,20 @@ def round_mask(S, W, N: int, M: int, ls_steps: int, out=None, stream=None):
 
 
 def mask_batched(items, tau: float, iters: int, ls_steps: int, return_frac: bool = False,
-                 outs=None, stream=None):
+                 outs=None, stream=None, polish_steps: int = 0, prev_masks=None):
     """Many matrices in one call (one launch per N:M and dtype class).
     items: iterable of (W, N, M); outs: optional list of mask buffers, one per
-    item.  Returns a list of (mask, frac_or_None) in the same order."""
+    item.  polish_steps and prev_masks (a list with one previous mask or None
+    per item; an entry may be the item's output buffer) add tsenor_mask_ex's
+    optional stages.  Returns a list of (mask, frac_or_None) in the same order."""
     torch = _torch()
     items = list(items)
     if outs is not None and len(outs) != len(items):
         raise ValueError("outs must hold one mask buffer per item")
+    if prev_masks is not None and len(prev_masks) != len(items):
+        raise ValueError("prev_masks must hold one entry (a mask or None) per item")
     arr = (_Matrix * max(1, len(items)))()
+    prevs = (_P * max(1, len(items)))()
     res = []
     for k, (W, N, M) in enumerate(items):
         dt = _weights(W)
@@ -260,11 +268,21 @@ def mask_batched(items, tau: float, iters: int, ls_steps: int, return_frac: bool
         f = torch.empty((rows, cols), dtype=torch.float32, device=W.device) if return_frac else None
         arr[k] = _Matrix(W.data_ptr(), dt, rows, cols, W.stride(0), N, M, m.data_ptr(),
                          f.data_ptr() if f is not None else 0)
+        if prev_masks is not None and prev_masks[k] is not None:
+            prevs[k] = _mask_buffer(W, prev_masks[k]).data_ptr()  # same checks as an output
         res.append((m, f))
-    st = lib().tsenor_mask_batched(arr, len(items), float(tau), int(iters), int(ls_steps),
-                                   _stream(stream))
+    if polish_steps == 0 and prev_masks is None:
+        st = lib().tsenor_mask_batched(arr, len(items), float(tau), int(iters), int(ls_steps),
+                                       _stream(stream))
+        where = "tsenor_mask_batched"
+    else:
+        st = lib().tsenor_mask_batched_ex(arr, len(items), float(tau), int(iters), int(ls_steps),
+                                          int(polish_steps),
+                                          prevs if prev_masks is not None else None,
+                                          _stream(stream))
+        where = "tsenor_mask_batched_ex"
     if st != 0:
-        raise TsenorError(st, "tsenor_mask_batched")
+        raise TsenorError(st, where)
     return res
 
 

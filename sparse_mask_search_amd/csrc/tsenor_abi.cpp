@@ -146,6 +146,27 @@ int ensure_scratch(DeviceState& st, size_t slots) {
     return TSENOR_OK;
 }
 
+// Ensure the cached copy buffer for previous masks holds `words` words.
+// Growing waits for every earlier launch that may still read the old buffer.
+int ensure_prev_copy(DeviceState& st, size_t words) {
+    if (st.prev_cap >= words) return TSENOR_OK;
+    hipError_t e;
+    if (st.prev_copy != nullptr) {
+        e = hipEventSynchronize(st.last);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        (void)hipFree(st.prev_copy);
+        st.prev_copy = nullptr;
+        st.prev_cap = 0;
+    }
+    e = hipMalloc(&st.prev_copy, words * sizeof(uint32_t));
+    if (e != hipSuccess) {
+        st.prev_copy = nullptr;
+        return hip_fail(e, "hipMalloc(previous mask copy)");
+    }
+    st.prev_cap = words;
+    return TSENOR_OK;
+}
+
 int64_t clamp_grid(int64_t groups, int num_cu, int occ) {
     int64_t cap = (int64_t)num_cu * (occ > 0 ? occ : 1);
     return groups < cap ? groups : cap;
@@ -237,20 +258,10 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
     prm.scratch = st->scratch;
     const bool refine = polish_steps > 0 || prev_mask != nullptr;
     const size_t words = (size_t)rows * (size_t)job.wpr;
-    if (prev_mask != nullptr && prev_mask == mask_out && st->prev_cap < words) {
-        // the previous mask is overwritten by the solve: keep a copy
-        hipError_t e = hipSuccess;
-        if (st->prev_copy != nullptr) {
-            e = hipEventSynchronize(st->last);
-            if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-            (void)hipFree(st->prev_copy);
-            st->prev_copy = nullptr;
-            st->prev_cap = 0;
-        }
-        e = hipMalloc(&st->prev_copy, words * sizeof(uint32_t));
-        if (e != hipSuccess) return hip_fail(e, "hipMalloc(previous mask copy)");
-        st->prev_cap = words;
-    }
+    // a previous mask that the solve overwrites is copied first
+    if (prev_mask != nullptr && prev_mask == mask_out &&
+        (st_code = ensure_prev_copy(*st, words)) != TSENOR_OK)
+        return st_code;
     if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
     hipError_t e;
     if (prev_mask != nullptr && prev_mask == mask_out) {
@@ -367,7 +378,13 @@ int tsenor_round(const float* S, int64_t lds, const void* W, int dtype, int64_t 
 
 int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int iters, int ls_steps,
                         void* stream) {
-    if (count < 0) return TSENOR_ERR_PARAM;
+    return tsenor_mask_batched_ex(mats, count, tau, iters, ls_steps, 0, nullptr, stream);
+}
+
+int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int iters,
+                           int ls_steps, int polish_steps, const uint32_t* const* prev_masks,
+                           void* stream) {
+    if (count < 0 || polish_steps < 0) return TSENOR_ERR_PARAM;
     if (count > 0 && mats == nullptr) return TSENOR_ERR_NULL;
     int st_code = check_params(tau, iters, ls_steps);
     if (st_code != TSENOR_OK) return st_code;
@@ -435,6 +452,14 @@ int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int ite
             cls[ncls++] = c;
         }
     if ((st_code = ensure_scratch(*st, (size_t)max_grid)) != TSENOR_OK) return st_code;
+    // previous masks that the solve overwrites are copied first, back to back
+    size_t alias_words = 0;
+    if (prev_masks != nullptr)
+        for (int i = 0; i < count; ++i)
+            if (prev_masks[i] != nullptr && prev_masks[i] == mats[i].mask_out)
+                alias_words += (size_t)mats[i].rows * (size_t)((mats[i].cols + 31) / 32);
+    if (alias_words > 0 && (st_code = ensure_prev_copy(*st, alias_words)) != TSENOR_OK)
+        return st_code;
     Params prm;
     prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
     prm.iters = iters;
@@ -444,6 +469,23 @@ int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int ite
     e = hipMemcpyAsync(st->jobs_dev, st->jobs_host, sizeof(MatJob) * (size_t)count,
                        hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
+    std::vector<const uint32_t*> prev_eff(count, nullptr);
+    if (prev_masks != nullptr) {
+        size_t off = 0;
+        for (int i = 0; i < count; ++i) {
+            prev_eff[i] = prev_masks[i];
+            if (prev_masks[i] == nullptr || prev_masks[i] != mats[i].mask_out) continue;
+            const size_t words = (size_t)mats[i].rows * (size_t)((mats[i].cols + 31) / 32);
+            e = hipMemcpyAsync(st->prev_copy + off, prev_masks[i], words * sizeof(uint32_t),
+                               hipMemcpyDeviceToDevice, s);
+            if (e != hipSuccess) {
+                (void)record_end(*st, s);
+                return hip_fail(e, "hipMemcpyAsync(previous mask)");
+            }
+            prev_eff[i] = st->prev_copy + off;
+            off += words;
+        }
+    }
     // The launches run in stream order, so they share the workspace.
     for (int k = 0; k < ncls; ++k) {
         const Class& c = cls[k];
@@ -453,6 +495,21 @@ int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int ite
             // earlier classes may be in flight: keep the workspace ordering
             (void)record_end(*st, s);
             return hip_fail(e, "batched kernel launch");
+        }
+    }
+    // optional stages, one refine launch per matrix that has any
+    for (int i = 0; i < count && (polish_steps > 0 || prev_masks != nullptr); ++i) {
+        if (polish_steps == 0 && prev_eff[i] == nullptr) continue;
+        const tsenor_matrix& m = mats[i];
+        MatJob job = make_job(m.W, m.dtype, m.rows, m.cols, m.ld, m.N, m.M, m.mask_out, nullptr);
+        job.prev = prev_eff[i];
+        const int64_t per_pass = tsenor::kWave / m.M;
+        const int64_t groups = (m.rows / m.M) * ((m.cols / m.M + per_pass - 1) / per_pass);
+        const int64_t rgrid = clamp_grid(groups, st->num_cu, st->occ_refine[job.bf16][m.M]);
+        e = (hipError_t)tsenor::launch_refine(job, polish_steps, (int)rgrid, stream);
+        if (e != hipSuccess) {
+            (void)record_end(*st, s);
+            return hip_fail(e, "refine kernel launch");
         }
     }
     return record_end(*st, s);

@@ -26,8 +26,8 @@ def declared():
 def test_exports_every_declared_symbol():
     names = declared()
     assert names == ["tsenor_compress24", "tsenor_exact", "tsenor_last_error", "tsenor_mask",
-                     "tsenor_mask_batched", "tsenor_mask_ex", "tsenor_round", "tsenor_spmm24",
-                     "tsenor_status_str", "tsenor_version"]
+                     "tsenor_mask_batched", "tsenor_mask_batched_ex", "tsenor_mask_ex",
+                     "tsenor_round", "tsenor_spmm24", "tsenor_status_str", "tsenor_version"]
     out = subprocess.check_output(["nm", "-D", "--defined-only", sms.library_path()], text=True)
     exported = set(re.findall(r"\bT (tsenor_\w+)", out))
     for n in names:
@@ -127,6 +127,11 @@ def test_batched_rejects():
     assert l.tsenor_mask_batched(arr, 1, -2.0, 5, 2, None) == PARAM
     assert l.tsenor_mask_batched(arr, 1, 20.0, 0, 2, None) == PARAM
     assert l.tsenor_mask_batched(None, 0, 20.0, 5, 2, None) == OK  # empty batch: no-op
+    # the extended form validates the same way, plus polish_steps
+    assert l.tsenor_mask_batched_ex(arr, 2, 20.0, 5, 2, 0, None, None) == SHAPE
+    assert l.tsenor_mask_batched_ex(arr, 1, 20.0, 5, 2, -1, None, None) == PARAM
+    assert l.tsenor_mask_batched_ex(None, 3, 20.0, 5, 2, 4, None, None) == NULL
+    assert l.tsenor_mask_batched_ex(None, 0, 20.0, 5, 2, 4, None, None) == OK
 
 
 def test_binding_requires_device_tensors():

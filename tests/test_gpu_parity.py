@@ -349,6 +349,51 @@ def test_batched_mixed_classes():
                       - S64).max() < S_TOL
 
 
+def test_batched_ex_equals_per_matrix_ex():
+    """tsenor_mask_batched_ex over a batch of every (M, dtype) class, with the
+    polish and with previous masks (one aliasing its output buffer, one
+    absent, the others separate), equals tsenor_mask_ex per matrix and the
+    oracle's extended rounding of the GPU's own S."""
+    import torch
+    rng = np.random.default_rng(78)
+    specs = [(32, 16, 64, 96, "bf16"), (4, 2, 8, 36, "f32"), (16, 8, 48, 80, "bf16"),
+             (8, 3, 24, 40, "f32"), (16, 5, 32, 48, "f32")]
+    tau, iters, ls, K = 25.0, 40, 6, 5
+    _note("batched_ex mixed classes")
+    items, bits, originals, prevs, outs = [], [], [], [], []
+    for k, (M, N, rows, cols, dt) in enumerate(specs):
+        W = (0.02 * rng.standard_t(3, (rows, cols))).astype(np.float32)
+        Wn = wl.f32_to_bf16_bits(W) if dt == "bf16" else W
+        Wt = to_device(Wn)
+        items.append((Wt, N, M))
+        bits.append(Wn)
+        # a previous mask polished further than this call will polish
+        p, _ = sms.mask(Wt, N, M, tau, iters, ls, polish_steps=60)
+        p = p.clone()
+        p[::5, 0] ^= 1  # some blocks infeasible: they ignore it
+        originals.append(None if k == 2 else p.clone())
+        out = p.clone()
+        outs.append(out)
+        prevs.append(out if k == 0 else (None if k == 2 else p))  # k = 0 aliases its output
+    res = sms.mask_batched(items, tau, iters, ls, return_frac=True, outs=outs,
+                           polish_steps=K, prev_masks=prevs)
+    torch.cuda.synchronize()
+    kept = 0
+    for (Wt, N, M), Wn, orig, (m, f) in zip(items, bits, originals, res):
+        rows, cols = Wt.shape
+        m1, f1 = sms.mask(Wt, N, M, tau, iters, ls, return_frac=True, polish_steps=K,
+                          prev_mask=orig)
+        torch.cuda.synchronize()
+        assert torch.equal(m, m1) and torch.equal(f, f1), (N, M)
+        assert_feasible(words(m), rows, cols, N, M)
+        ref, st = oracle.round_matrix_ex(f.cpu().numpy(), as_f32(Wn), N, M, ls, K,
+                                         prev_mask=None if orig is None else words(orig))
+        assert np.array_equal(words(m), ref), (N, M)
+        kept += int(st[5])
+    print(f"blocks that kept the previous mask: {kept}", flush=True)
+    assert kept > 0
+
+
 def test_output_buffers_are_checked():
     """Caller-supplied mask / frac buffers of the wrong shape, dtype or layout
     are refused before anything is enqueued."""
