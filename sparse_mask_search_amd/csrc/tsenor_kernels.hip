@@ -1145,6 +1145,20 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
 }
 
 // ---------------------------------------------------------------- refine
+// LDS of the refine pass: |W| rows, mask rows, then per block a triangular
+// table of the best swap of every row pair (8-byte keys), an area the
+// keep-better sums reuse.
+template <int M> constexpr int kPairs = M * (M - 1) / 2;
+template <int M>
+__device__ __forceinline__ int tri(int a, int b) { return a * M - a * (a + 1) / 2 + (b - a - 1); }
+template <int M> constexpr int ref_tab_offset() {  // in floats, 8-byte aligned
+    return ((kWave / M) * M * (M + 1) + kWave + 1) & ~1;
+}
+template <int M> constexpr int ref_lds_floats() {
+    constexpr int tabs = 2 * (kWave / M) * kPairs<M>, sums = 2 * 2 * kWave;
+    return ref_tab_offset<M>() + (tabs > sums ? tabs : sums);
+}
+
 // Optional stages on a finished mask (job.mask), for the 64/M blocks of one
 // pass: lane (q, i) = block q, row i.  |W| rows are staged in LDS like the
 // rounding's; the result is written back to job.mask.
@@ -1157,9 +1171,11 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
     asm volatile("" : "+v"(lane));
     const int q = lane / M, i = lane % M;
     const int N = job.N;
-    float* Ss = lds;                                                     // scratch for R5
-    float* As = lds + G * kStageBlk<M>;                                  // [G][M][M+1]
-    uint32_t* Zs = reinterpret_cast<uint32_t*>(As + G * M * (M + 1));  // [G][M]
+    // LDS: |W| rows [G][M][M+1], mask rows [G][M], then the polish's pair
+    // tables (the R5 sums reuse that area once the polish is done)
+    float* As = lds;
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(As + G * M * (M + 1));
+    uint64_t* tab_area = reinterpret_cast<uint64_t*>(lds + ref_tab_offset<M>());
     uint32_t Z = 0u;
     {
         float a[M];
@@ -1190,7 +1206,8 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
         // once; after a swap of rows r1, r2 only the pairs touching r1 or r2
         // change, and lane p re-evaluates {p, r1} and {p, r2} -- two pairs per
         // lane per step.
-        uint64_t* tab = reinterpret_cast<uint64_t*>(Zs + G * M) + q * M * M;  // [M][M], a < b
+        // triangular: pair {a < b} at tri<M>(a, b); row a's pairs are contiguous
+        uint64_t* tab = tab_area + q * kPairs<M>;
         float ai[M];
         {
             const float* Ai = As + (q * M + i) * (M + 1);
@@ -1219,24 +1236,26 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
             }
             const float G = __fadd_rn(T1, -Dmin);
             if (dj == 0u || !(G > 0.f)) return 0ull;
-            int jb = M;
-            float t2 = 0.f;
+            // smallest j attaining G, then the smallest j' given that j: bit
+            // masks of the hits, then their lowest bit
+            uint32_t hj = 0u;
 #pragma unroll
             for (int c = 0; c < M; ++c) {
                 const float x = __fsub_rn(ai[c], Ap[c]);
                 const float d = lo ? x : -x;
-                const bool hit = jb == M && ((dj >> c) & 1u) && __fadd_rn(T1, -d) == G;
-                jb = hit ? c : jb;
-                t2 = hit ? -d : t2;
+                hj |= (__fadd_rn(T1, -d) == G) ? (1u << c) : 0u;
             }
-            int jpb = M;
+            const int jb = __ffs(hj & dj) - 1;
+            const float xb = __fsub_rn(As[(q * M + i) * (M + 1) + jb], Ap[jb]);
+            const float t2 = lo ? -xb : xb;  // -d_jb
+            uint32_t hk = 0u;
 #pragma unroll
             for (int c = 0; c < M; ++c) {
                 const float x = __fsub_rn(ai[c], Ap[c]);
                 const float d = lo ? x : -x;
-                const bool hit = jpb == M && ((dk >> c) & 1u) && __fadd_rn(d, t2) == G;
-                jpb = hit ? c : jpb;
+                hk |= (__fadd_rn(d, t2) == G) ? (1u << c) : 0u;
             }
+            const int jpb = __ffs(hk & dk) - 1;
             const int a = lo ? i : p, b = lo ? p : i;
             const uint32_t lex = (uint32_t)(((a * M + jb) * M + b) * M + jpb);
             return ((uint64_t)float_to_ord(G) << 32) | (uint64_t)(0xFFFFFFFFu - lex);
@@ -1247,18 +1266,17 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
             const int p = (i + k) % M;
             if (k < M / 2 || i < M / 2) {
                 const int a = i < p ? i : p, b = i < p ? p : i;
-                tab[a * M + b] = valid ? pair_key(p, Zs[q * M + p]) : 0ull;
+                tab[tri<M>(a, b)] = valid ? pair_key(p, Zs[q * M + p]) : 0ull;
             }
         }
         __syncthreads();
         bool active = valid;
         for (int step = 0; step < polish_steps && __ballot(active) != 0ull; ++step) {
             uint64_t best = 0;
-            for (int p = 1; p < M; ++p) {
-                if (p > i) {
-                    const uint64_t k = tab[i * M + p];
-                    best = k > best ? k : best;
-                }
+            const uint64_t* row = tab + tri<M>(i, i + 1);
+            for (int p = i + 1; p < M; ++p) {
+                const uint64_t k = row[p - i - 1];
+                best = k > best ? k : best;
             }
             if (!active) best = 0ull;
             best = group_max_u64<M>(best);
@@ -1285,11 +1303,11 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
                 const int pb = (i == r1 || i == r2) ? -1 : r2;
                 {
                     const int lo2 = i < pa ? i : pa, hi2 = i < pa ? pa : i;
-                    if (i != r2 || pa != r1) tab[lo2 * M + hi2] = pair_key(pa, Zs[q * M + pa]);
+                    if (i != r2 || pa != r1) tab[tri<M>(lo2, hi2)] = pair_key(pa, Zs[q * M + pa]);
                 }
                 if (pb >= 0) {
                     const int lo2 = i < pb ? i : pb, hi2 = i < pb ? pb : i;
-                    tab[lo2 * M + hi2] = pair_key(pb, Zs[q * M + pb]);
+                    tab[tri<M>(lo2, hi2)] = pair_key(pb, Zs[q * M + pb]);
                 }
             }
             __syncthreads();
@@ -1317,7 +1335,7 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
             if ((Z >> j) & 1u) rz += a;
             if ((Zp >> j) & 1u) rp += a;
         }
-        double* sums = reinterpret_cast<double*>(Ss);  // [G][M][2]; staging area is free now
+        double* sums = reinterpret_cast<double*>(tab_area);  // [G][M][2]; tables are done
         sums[2 * (q * M + i)] = rz;
         sums[2 * (q * M + i) + 1] = rp;
         __syncthreads();
@@ -1337,12 +1355,6 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
     if constexpr (M <= 8) w |= xor_lane<8>(w);
     if constexpr (M <= 16) w |= xor_lane<16>(w);
     if (valid && bit0 == 0) job.mask[(br * M + i) * job.wpr + ((bc * M) >> 5)] = w;
-}
-
-// Refine LDS: the rounding's staging areas, then the pair table of the polish
-// (M*M keys of 8 bytes per block).
-template <int M> constexpr int ref_lds_floats() {
-    return rnd_lds_floats<M>() + 2 * (kWave / M) * M * M + 2;
 }
 
 template <int M, bool BF16>
