@@ -94,8 +94,8 @@ int tsenor_mask(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld
                 float tau, int iters, int ls_steps, uint32_t* mask_out, float* frac_out,
                 void* stream);
 
-/* tsenor_mask followed by two optional stages per block (not on the pages; the
- * survey of the method ranks them first among the next steps):
+/* tsenor_mask followed by two optional stages per block (not part of the
+ * method as the pages describe it):
  *   polish_steps  >= 0: at most this many 2-opt swaps after the fill.  A swap
  *            takes kept (i, j) and (i', j'), i < i', with Z_ij' = Z_i'j = 0, to
  *            (i, j') and (i', j), keeping every row and column count; its gain

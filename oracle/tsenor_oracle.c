@@ -11,7 +11,7 @@
  * Algorithm for Finding Transposable N:M Sparse Masks" (Meng, Makni, Mazumder,
  * arXiv 2505.23949) -- sections "What carries the argument" and "Extended
  * reading notes / Core claim".  Where that page leaves a step open, the reading
- * taken is written next to the step (readings c1..c18 in the design notes).
+ * taken is stated next to the step.
  *
  * Precision: every Dykstra quantity is fp64 with natural logarithms; the
  * rounding stage consumes the fp32 fractional matrix S32 and scores moves in
@@ -48,10 +48,12 @@ static void gather_abs(const float* W, int64_t ld, int64_t bi, int64_t bj, int M
 /* ------------------------------------------------------------------------ */
 /* Entropic capacitated OT by Dykstra's alternating KL projections, log space
  * ("What carries the argument"; "Core claim"):
- *   scores  What = A / max(A)  (max over the block; an all-zero block gives
- *           What = 0)                                          [reading c2]
- *   start   X = tau * What, Q = 0   (Gibbs kernel exp(tau*What))  [c1, c6]
- *   repeat T times, in this order                               [c4, c5, c7]
+ *   scores  What = A / max(A)  (max over the block -- the page leaves the
+ *           normalisation open; an all-zero block gives What = 0)
+ *   start   X = tau * What, Q = 0   (the Gibbs kernel exp(tau*What); tau
+ *           multiplies the normalised scores)
+ *   repeat T times, in this order (one cycle = C1, C2, C3; exactly T cycles,
+ *   no stopping test)
  *     C1  row normalisation:    X_ij += ln N - LSE_j' X_ij'
  *     C2  column normalisation: X_ij += ln N - LSE_i' X_i'j
  *     C3  clip at 1 with the Dykstra correction:
@@ -106,15 +108,18 @@ static int dykstra_block(const float* A, int N, int M, double tau, int iters,
 /* Rounding ("What carries the argument": sort descending, greedy within the
  * row/column budgets, then a local search on the swap score).
  *
- * R1 greedy   order all M^2 entries by (S32 descending, i*M+j ascending)
- *             [c9]; accept (i,j) iff r_i < N and c_j < N [c10].
- * R2 search   (<= L moves) [c11]: over every deficient row i, deficient
+ * R1 greedy   order all M^2 entries by (S32 descending, i*M+j ascending: the
+ *             page gives no tie rule); accept (i,j) iff r_i < N and c_j < N.
+ * R2 search   (<= L moves; one move per step, the best over all deficient
+ *             pairs -- the page fixes neither): over every deficient row i, deficient
  *             column j and (i',j') with Z_i'j' = 1, Z_ij' = 0, Z_i'j = 0,
- *             score = fl32(fl32(A_ij' + A_i'j) - A_i'j') [c13]; take the
+ *             score = fl32(fl32(A_ij' + A_i'j) - A_i'j') on raw |W|; take the
  *             maximum, ties to the smallest (i, j, i', j'); apply the move
  *             (set Z_ij' = Z_i'j = 1, clear Z_i'j') only if score > 0, else
  *             stop.
- * R3 fill     [c12] while a shortfall remains: i = smallest deficient row,
+ * R3 fill     (not on the page; it runs after the search, which only has
+ *             work while a shortfall remains) while a shortfall remains:
+ *             i = smallest deficient row,
  *             j = smallest deficient column; best (i',j') by the same score,
  *             ties to the smallest (i', j'); apply with no sign condition.
  * Invariant I (checked): Z_ij = 1 for every deficient row i and deficient
@@ -239,8 +244,8 @@ static int round_block(const float* S, const float* A, int N, int M, int L,
 }
 
 /* ------------------------------------------------------------------------ */
-/* Optional stages after R3 (the survey's "next" row f1; the pages describe no
- * such step -- readings r4/r5 in the design notes):
+/* Optional stages after R3 (the pages describe no such step; the readings
+ * below are this oracle's own):
  *
  * R4 2-opt polish, at most K swaps.  A swap takes kept (i, j) and (i', j'),
  *    i < i', with Z_ij' = Z_i'j = 0, to (i, j') and (i', j); every row and
@@ -504,7 +509,7 @@ int oracle_round_block(const float* S32, const float* A, int N, int M, int ls_st
 /* Rounding of every block of a matrix.  S32 [rows x cols] with leading
  * dimension lds; W [rows x cols] with leading dimension ld (A = |W|).  The
  * mask is packed row-major into uint32 words, ceil(cols/32) words per row,
- * bit (c % 32) of word c / 32 is column c [reading c18].  stats (may be NULL)
+ * bit (c % 32) of word c / 32 is column c (the page fixes no layout).  stats (may be NULL)
  * accumulates [blocks with D > 0, total D, R2 moves, R3 moves].             */
 int oracle_round(const float* S32, int64_t lds, const float* W, int64_t ld,
                  int64_t rows, int64_t cols, int N, int M, int ls_steps,

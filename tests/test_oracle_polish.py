@@ -1,7 +1,7 @@
 """Pins of the oracle's optional stages after the fill: the 2-opt polish (R4)
 and the keep-better safeguard against a previous mask (R5).
 
-These stages are not on the pages (the survey's "next" row f1); their reading:
+These stages are not on the pages; their reading:
 a swap takes kept (i, j), (i', j'), i < i', with Z_ij' = Z_i'j = 0, to (i, j'),
 (i', j); gain (A_ij' - A_i'j') + (A_i'j - A_ij) in fp32; best gain, ties to the
 smallest (i, j, i', j'), applied only if > 0; the safeguard keeps a feasible
