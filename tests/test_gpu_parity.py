@@ -169,6 +169,37 @@ def test_power_of_two_scale_invariance(M, bf16, k):
     assert np.array_equal(S1, S2)
 
 
+@pytest.mark.parametrize("seed", [11, 12, 13])
+def test_random_configurations(seed):
+    """Seeded random mixes of M, N (1..M), value distribution, tau (0..150),
+    cycles (1..80), local-search steps (0..64) and dtype: S within the
+    contract of the fp64 oracle, masks bit-exact with the oracle's rounding of
+    the GPU's S, for the fused path and the rounding-only entry point."""
+    import torch
+    rng = np.random.default_rng(seed)
+    for case in range(40):
+        M = int(rng.choice([4, 8, 16, 32]))
+        N = int(rng.integers(1, M + 1))
+        nbc, nbr = int(rng.integers(1, 12)), int(rng.integers(1, 3))
+        kind = str(rng.choice(["normal", "outlier", "student_t", "ties", "uniform"]))
+        tau = float(rng.choice([0.0, 5.0, 20.0, 60.0, 150.0]))
+        T = int(rng.choice([1, 2, 5, 20, 80]))
+        L = int(rng.choice([0, 1, 3, 8, 64]))
+        bf16 = bool(rng.integers(0, 2))
+        W = np.concatenate([wl.random_blocks(seed * 10000 + 100 * case + r, nbc, M, kind)
+                            for r in range(nbr)]).astype(np.float32)
+        Wn = wl.f32_to_bf16_bits(W) if bf16 else W
+        _note(f"random seed={seed} case={case}: M={M} N={N} {W.shape} {kind} tau={tau} "
+              f"T={T} L={L} bf16={bf16}")
+        _, mask, S, mask2 = _run(Wn, N, M, tau, T, L)
+        Wf = as_f32(Wn)
+        S64, _ = oracle.dykstra(Wf, N, M, tau, T)
+        assert np.abs(S - S64).max() < S_TOL
+        ref, _ = oracle.round_matrix(S, Wf, N, M, L)
+        assert np.array_equal(mask, ref) and np.array_equal(mask2, ref)
+        assert_feasible(mask, *W.shape, N, M)
+
+
 @pytest.mark.parametrize("M", [4, 8, 16, 32])
 def test_closed_forms(M):
     """tau = 0: S = N/M everywhere and the mask is the block diagonal of N x N
