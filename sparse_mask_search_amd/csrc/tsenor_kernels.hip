@@ -1146,7 +1146,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
 
 // ---------------------------------------------------------------- refine
 // LDS of the refine pass: |W| rows, mask rows, then per block a triangular
-// table of the best swap of every row pair (8-byte keys), an area the
+// table of the best swap gain of every row pair (4-byte keys), an area the
 // keep-better sums reuse.
 template <int M> constexpr int kPairs = M * (M - 1) / 2;
 template <int M>
@@ -1155,7 +1155,7 @@ template <int M> constexpr int ref_tab_offset() {  // in floats, 8-byte aligned
     return ((kWave / M) * M * (M + 1) + kWave + 1) & ~1;
 }
 template <int M> constexpr int ref_lds_floats() {
-    constexpr int tabs = 2 * (kWave / M) * kPairs<M>, sums = 2 * 2 * kWave;
+    constexpr int tabs = (kWave / M) * kPairs<M>, sums = 2 * 2 * kWave;
     return ref_tab_offset<M>() + (tabs > sums ? tabs : sums);
 }
 
@@ -1201,13 +1201,14 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
     // max over j of the second; the smallest j and then j' attaining it give
     // the lexicographic tie-break.
     if (polish_steps > 0) {
-        // Pair table: the best swap of every row pair {a < b} of the block as a
-        // packed (fp32 gain, ~lexicographic index) key, 0 = none.  It is filled
-        // once; after a swap of rows r1, r2 only the pairs touching r1 or r2
-        // change, and lane p re-evaluates {p, r1} and {p, r2} -- two pairs per
-        // lane per step.
-        // triangular: pair {a < b} at tri<M>(a, b); row a's pairs are contiguous
-        uint64_t* tab = tab_area + q * kPairs<M>;
+        // Gain table: for every row pair {a < b} of the block, the ordered key
+        // of its best swap gain (0 = no improving swap), triangular, pair at
+        // tri<M>(a, b), so row a's pairs are contiguous.  Filled once; after a
+        // swap of rows r1, r2 only the pairs touching r1 or r2 change, and lane
+        // p re-evaluates {p, r1} and {p, r2} -- two pairs per lane per step.
+        // Which (j, j') attains a pair's gain matters only for the pairs tied
+        // at a step's best gain, so it is found then, for those pairs alone.
+        uint32_t* tab = reinterpret_cast<uint32_t*>(tab_area) + q * kPairs<M>;
         float ai[M];
         {
             const float* Ai = As + (q * M + i) * (M + 1);
@@ -1216,17 +1217,18 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
         }
         Zs[q * M + i] = Z;
         __syncthreads();
-        // Best swap of the pair {i, p} (p != i), row p's mask Zp: with a =
-        // min(i, p), b = max(i, p), d_c = fl(A_ac - A_bc) = +-fl(A_ic - A_pc),
-        // the second difference is fl(A_bj - A_aj) = -d_j exactly, so the best
-        // gain is fl(T1 - min over j of d_j), T1 = max over j' of d_j'.
-        auto pair_key = [&](int p, uint32_t Zp) -> uint64_t {
+        // The pair {i, p} (p != i), row p's mask Zp: with a = min(i, p), b =
+        // max(i, p), d_c = fl(A_ac - A_bc) = +-fl(A_ic - A_pc), the second
+        // difference is fl(A_bj - A_aj) = -d_j exactly, so the best gain is
+        // fl(T1 - min over j of d_j), T1 = max over j' of d_j'.
+        auto pair_gain = [&](int p, uint32_t Zp, float& T1) -> float {
             const bool lo = i < p;
             const uint32_t Za = lo ? Z : Zp, Zb = lo ? Zp : Z;
             const uint32_t dj = Za & ~Zb;   // j:  Z_aj = 1, Z_bj = 0
             const uint32_t dk = Zb & ~Za;   // j': Z_bj' = 1, Z_aj' = 0
             const float* Ap = As + (q * M + p) * (M + 1);
-            float T1 = -__builtin_inff(), Dmin = __builtin_inff();
+            float Dmin = __builtin_inff();
+            T1 = -__builtin_inff();
 #pragma unroll
             for (int c = 0; c < M; ++c) {
                 const float x = __fsub_rn(ai[c], Ap[c]);
@@ -1234,10 +1236,23 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
                 if ((dk >> c) & 1u) T1 = fmaxf(T1, d);
                 if ((dj >> c) & 1u) Dmin = fminf(Dmin, d);
             }
-            const float G = __fadd_rn(T1, -Dmin);
-            if (dj == 0u || !(G > 0.f)) return 0ull;
-            // smallest j attaining G, then the smallest j' given that j: bit
-            // masks of the hits, then their lowest bit
+            return dj == 0u ? -__builtin_inff() : __fadd_rn(T1, -Dmin);
+        };
+        auto gain_key = [&](int p, uint32_t Zp) -> uint32_t {
+            float T1;
+            const float G = pair_gain(p, Zp, T1);
+            return G > 0.f ? float_to_ord(G) : 0u;
+        };
+        // (a, j, b, j') of the pair {i, p} at gain G: the smallest j attaining
+        // G, then the smallest j' given that j (bit masks of the hits, lowest
+        // bit), as one lexicographic index
+        auto pair_lex = [&](int p, uint32_t Zp, float G) -> uint32_t {
+            const bool lo = i < p;
+            const uint32_t Za = lo ? Z : Zp, Zb = lo ? Zp : Z;
+            const uint32_t dj = Za & ~Zb, dk = Zb & ~Za;
+            const float* Ap = As + (q * M + p) * (M + 1);
+            float T1;
+            (void)pair_gain(p, Zp, T1);
             uint32_t hj = 0u;
 #pragma unroll
             for (int c = 0; c < M; ++c) {
@@ -1257,8 +1272,7 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
             }
             const int jpb = __ffs(hk & dk) - 1;
             const int a = lo ? i : p, b = lo ? p : i;
-            const uint32_t lex = (uint32_t)(((a * M + jb) * M + b) * M + jpb);
-            return ((uint64_t)float_to_ord(G) << 32) | (uint64_t)(0xFFFFFFFFu - lex);
+            return (uint32_t)(((a * M + jb) * M + b) * M + jpb);
         };
         // Fill: lane i takes the partners i+1 .. i+M/2 (mod M), the last one only
         // for i < M/2 -- every pair exactly once, about M/2 pairs per lane.
@@ -1266,35 +1280,48 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
             const int p = (i + k) % M;
             if (k < M / 2 || i < M / 2) {
                 const int a = i < p ? i : p, b = i < p ? p : i;
-                tab[tri<M>(a, b)] = valid ? pair_key(p, Zs[q * M + p]) : 0ull;
+                tab[tri<M>(a, b)] = valid ? gain_key(p, Zs[q * M + p]) : 0u;
             }
         }
         __syncthreads();
         bool active = valid;
         for (int step = 0; step < polish_steps && __ballot(active) != 0ull; ++step) {
-            uint64_t best = 0;
-            const uint64_t* row = tab + tri<M>(i, i + 1);
-            for (int p = i + 1; p < M; ++p) {
-                const uint64_t k = row[p - i - 1];
-                best = k > best ? k : best;
+            // the best gain of the block: lane i scans the pairs it fills
+            // (the same circulant share, about M/2 independent reads)
+            uint32_t g = 0u;
+#pragma unroll
+            for (int k = 1; k <= M / 2; ++k) {
+                const int p = (i + k) % M;
+                const int a = i < p ? i : p, b = i < p ? p : i;
+                const uint32_t v = (k < M / 2 || i < M / 2) ? tab[tri<M>(a, b)] : 0u;
+                g = v > g ? v : g;
             }
-            if (!active) best = 0ull;
-            best = group_max_u64<M>(best);
+            if (!active) g = 0u;
+            const uint32_t gmax = group_max_u32<M>(g);
+            if (active && gmax == 0u) active = false;  // no improving swap left
+            // the lexicographically smallest swap among the pairs at that gain
+            uint32_t lx = 0xFFFFFFFFu;
+            if (active && g == gmax) {
+                const float G = ord_to_float(gmax);
+                for (int k = 1; k <= M / 2; ++k) {
+                    const int p = (i + k) % M;
+                    const int a = i < p ? i : p, b = i < p ? p : i;
+                    if (!(k < M / 2 || i < M / 2) || tab[tri<M>(a, b)] != gmax) continue;
+                    const uint32_t l = pair_lex(p, Zs[q * M + p], G);
+                    lx = l < lx ? l : lx;
+                }
+            }
+            const uint32_t lex = group_min_u32<M>(lx);
             __syncthreads();
             int r1 = -1, r2 = -1;
             if (active) {
-                if (best == 0ull) {
-                    active = false;  // no improving swap left in this block
-                } else {
-                    const uint32_t lex = 0xFFFFFFFFu - (uint32_t)best;
-                    const int jp = (int)(lex % M), ip = (int)((lex / M) % M);
-                    const int j = (int)((lex / (M * M)) % M), ii = (int)(lex / (M * M * M));
-                    if (i == ii) Z = (Z & ~(1u << j)) | (1u << jp);
-                    if (i == ip) Z = (Z & ~(1u << jp)) | (1u << j);
-                    Zs[q * M + i] = Z;
-                    r1 = ii;
-                    r2 = ip;
-                }
+                const int jp = (int)(lex % M), ip = (int)((lex / M) % M);
+                const int j = (int)((lex / (M * M)) % M), ii = (int)(lex / (M * M * M));
+                if (i == ii) Z = (Z & ~(1u << j)) | (1u << jp);
+                if (i == ip) Z = (Z & ~(1u << jp)) | (1u << j);
+                Zs[q * M + i] = Z;
+                r1 = ii;
+                r2 = ip;
             }
             __syncthreads();
             if (r1 >= 0) {
@@ -1303,11 +1330,11 @@ __device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64
                 const int pb = (i == r1 || i == r2) ? -1 : r2;
                 {
                     const int lo2 = i < pa ? i : pa, hi2 = i < pa ? pa : i;
-                    if (i != r2 || pa != r1) tab[tri<M>(lo2, hi2)] = pair_key(pa, Zs[q * M + pa]);
+                    if (i != r2 || pa != r1) tab[tri<M>(lo2, hi2)] = gain_key(pa, Zs[q * M + pa]);
                 }
                 if (pb >= 0) {
                     const int lo2 = i < pb ? i : pb, hi2 = i < pb ? pb : i;
-                    tab[tri<M>(lo2, hi2)] = pair_key(pb, Zs[q * M + pb]);
+                    tab[tri<M>(lo2, hi2)] = gain_key(pb, Zs[q * M + pb]);
                 }
             }
             __syncthreads();
