@@ -83,6 +83,27 @@ __global__ void compress24_kernel(const uint16_t* __restrict__ W, int64_t ld,
     if (nbad && bad != nullptr) atomicAdd(bad, nbad);
 }
 
+// Output tile (tm, tn) of workgroup `bid` in a tiles_m x tiles_n grid.  The
+// hardware hands workgroups to the chip's 8 XCDs round robin (workgroup b runs
+// on XCD b % 8), and each XCD has its own L2.  When the grid divides by 8, XCD
+// x gets the contiguous tile range [x nb/8, (x+1) nb/8) of an order that walks
+// groups of up to 8 m-tiles column by column, so the tiles an XCD runs at one
+// time form a compact block of the grid: 32 concurrent tiles cover 8 m-tiles
+// (rows of A) by 4 n-tiles (rows of X, twice the bytes of an A tile) instead of
+// 2 by 16, and share those rows in the XCD's L2.  A bijection on [0, nb).
+__device__ __forceinline__ void tile_of_block(int64_t bid, int64_t tiles_m, int64_t tiles_n,
+                                              int64_t& tm, int64_t& tn) {
+    constexpr int64_t kXcd = 8, kGroupM = 8;
+    const int64_t nb = tiles_m * tiles_n;
+    const int64_t t = (nb % kXcd == 0) ? (bid % kXcd) * (nb / kXcd) + bid / kXcd : bid;
+    const int64_t per_group = kGroupM * tiles_n;
+    const int64_t grp = t / per_group, first = grp * kGroupM;
+    const int64_t gm = (tiles_m - first < kGroupM) ? tiles_m - first : kGroupM;
+    const int64_t r = t - grp * per_group;
+    tm = first + r % gm;
+    tn = r / gm;
+}
+
 // Y [n][m] fp32 (leading dimension ldy) = X [n][k] bf16 (ldx) times A^T, A
 // [m][k] compressed as above.  One workgroup of 4 waves per 128 x 128 tile of
 // (m, n); each wave owns 64 x 64 = 2 x 2 smfmac tiles and walks k in chunks of
@@ -94,8 +115,8 @@ __global__ __launch_bounds__(256) void spmm24_kernel(const uint16_t* __restrict_
                                                      int64_t m, int64_t k) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = lane >> 5, l32 = lane & 31;
-    const int64_t tiles_m = m / 128;
-    const int64_t tm = blockIdx.x % tiles_m, tn = blockIdx.x / tiles_m;
+    int64_t tm, tn;
+    tile_of_block(blockIdx.x, m / 128, n / 128, tm, tn);
     const int64_t m0 = tm * 128 + 64 * (wave >> 1), n0 = tn * 128 + 64 * (wave & 1);
     const int64_t chunks = k / 32;
     f32x16 acc[2][2];
@@ -195,7 +216,7 @@ __global__ __launch_bounds__(256) void spmm24_dma_kernel(const uint16_t* __restr
                                                          const uint16_t* __restrict__ vals,
                                                          const uint32_t* __restrict__ meta,
                                                          float* __restrict__ Y, int64_t ldy,
-                                                         int64_t m, int64_t k) {
+                                                         int64_t n, int64_t m, int64_t k) {
     constexpr int TM = 64 * WM, TN = 64 * WN;
     static_assert(TN % 32 == 0 && TM % 64 == 0, "tile");
     constexpr int QX = TN / 8 / 4;   // 1 KiB X instructions per wave per step (8 rows each)
@@ -208,8 +229,9 @@ __global__ __launch_bounds__(256) void spmm24_dma_kernel(const uint16_t* __restr
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
-    const int64_t tiles_m = m / TM;
-    const int64_t m0 = (blockIdx.x % tiles_m) * TM, n0 = (blockIdx.x / tiles_m) * TN;
+    int64_t tm, tn;
+    tile_of_block(blockIdx.x, m / TM, n / TN, tm, tn);
+    const int64_t m0 = tm * TM, n0 = tn * TN;
     const int64_t kh = k / 2, kw = k / 32;
     const int steps = (int)(k / 64);
 
@@ -349,7 +371,7 @@ int launch_spmm24(const uint16_t* X, int64_t ldx, const uint16_t* vals, const ui
         (reinterpret_cast<uintptr_t>(vals) & 15u) == 0) {
         const int64_t blocks = (m / TM) * (n / TN);
         hipLaunchKernelGGL((spmm24_dma_kernel<WM, WN>), dim3((unsigned)blocks), dim3(256), 0,
-                           (hipStream_t)stream, X, ldx, vals, meta, Y, ldy, m, k);
+                           (hipStream_t)stream, X, ldx, vals, meta, Y, ldy, n, m, k);
         return (int)hipGetLastError();
     }
     const int64_t blocks = (m / 128) * (n / 128);
