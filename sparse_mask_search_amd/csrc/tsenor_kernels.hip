@@ -240,16 +240,24 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// Sum / max of x over the H lanes that share a tile row (all lanes active).
+// Totals over the two lanes of a tile row (M = 32) for a pair of slots: the
+// partner lane holds the same two rows in the opposite slots, so slot 0 here
+// meets the partner's slot 1.
+template <bool MAXOP>
+__device__ __forceinline__ void row_pair_allreduce(float& x0, float& x1) {
+    static_assert(kBfly<32> && kH<32> == 2, "row halves pair by the butterfly layout");
+    const float y0 = dpp_mov<Lanes32::kRow>(x1), y1 = dpp_mov<Lanes32::kRow>(x0);
+    x0 = MAXOP ? fmaxf(x0, y0) : x0 + y0;
+    x1 = MAXOP ? fmaxf(x1, y1) : x1 + y1;
+}
+// Totals over the H lanes of a tile row for every slot of a lane.
 template <int M, bool MAXOP>
-__device__ __forceinline__ float row_allreduce(float x) {
+__device__ __forceinline__ void row_allreduce_slots(float (&x)[kR<M>]) {
+    static_assert(kH<M> == 1 || (kH<M> == 2 && kR<M> % 2 == 0), "H");
     if constexpr (kH<M> == 2) {
-        static_assert(kBfly<M>, "row halves pair by the butterfly layout");
-        const float y = dpp_mov<Lanes32::kRow>(x);
-        x = MAXOP ? fmaxf(x, y) : x + y;
+#pragma unroll
+        for (int r = 0; r < kR<M>; r += 2) row_pair_allreduce<MAXOP>(x[r], x[r + 1]);
     }
-    static_assert(kH<M> == 1 || kH<M> == 2, "H");
-    return x;
 }
 
 // Butterfly (M = 32): on return x[0..3] of every lane hold the column totals
@@ -281,12 +289,13 @@ __device__ __forceinline__ void col_all_gather(float (&x)[16]) {
 // of the block combines columns [lb*CPL, lb*CPL + CPL) over the G rows and
 // stores them to the block's broadcast row, from which every lane reads its
 // own CW columns.  KIND 0 broadcasts the totals (combine = max or sum);
-// KIND 1 turns each total C_j into V_j * N / C_j with V_j the value currently
-// in the broadcast row and, when `check` is set, returns whether any new V_j
-// of this lane left [2^-40, 2^40].
+// KIND 1 turns each total C_j into V_j / C_j with V_j the value currently in
+// the broadcast row (the cycle loop's column totals carry a factor 1/N, see
+// there) and, when `check` is set, returns whether any new V_j of this lane
+// left [2^-40, 2^40].
 template <int M, int KIND, bool MAXOP>
 __device__ __forceinline__ bool col_exchange(const float (&part)[kCW<M>], float (&out)[kCW<M>],
-                                             float* lds, int blk, int lb, float fN, bool check) {
+                                             float* lds, int blk, int lb, bool check) {
     constexpr int CW = kCW<M>, G = kG<M>, H = kH<M>, CPL = kCPL<M>;
     const int g = lb / H, h = lb % H;
     float* mine = lds + blk * kBlkStride<M> + g * kRowStride<M> + h * CW;
@@ -310,7 +319,7 @@ __device__ __forceinline__ bool col_exchange(const float (&part)[kCW<M>], float 
     bool bad = false;
     if constexpr (KIND == 1) {
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] = bc[lb * CPL + c] * (fN * rcpf(acc[c]));
+        for (int c = 0; c < CPL; ++c) acc[c] = bc[lb * CPL + c] * rcpf(acc[c]);
         if (check) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) bad |= !(acc[c] >= 0x1p-40f && acc[c] <= 0x1p40f);
@@ -355,6 +364,10 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     int g = lb / H, h = lb % H;
     if constexpr (kBfly<M>) { g = Lanes32::g(lb); h = Lanes32::h(lb); }
     const int sw = kBfly<M> ? g : 0;  // register quad k holds column quad k ^ sw
+    // Slot k of the lane's tile holds tile row k ^ rsw: the two lanes of a
+    // tile row (H = 2) hold each pair of rows in opposite slot order, so one
+    // exchange of partial sums and one reciprocal serve two rows.
+    const int rsw = (H == 2) ? h : 0;
     const int64_t nbc = job.cols / M;
     const int64_t bc = bc0 + blk;
     const bool valid = bc < nbc;
@@ -371,7 +384,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         if (valid) {
-            load_abs_row<CW, BF16>(job.W, (row0 + r) * job.ld + col0, vec, P[r]);
+            load_abs_row<CW, BF16>(job.W, (row0 + (r ^ rsw)) * job.ld + col0, vec, P[r]);
             if constexpr (kBfly<M>) permute_quads(P[r], sw);
         } else {
 #pragma unroll
@@ -394,18 +407,29 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 
     bool deep;
     // ---- cycle 1 in log2 space (Q = 0, so no clip enters C1/C2) ----
+    {  // C1: row max, then row sum of 2^(x - max)
+        float mx[R], sm[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {  // C1
-        float mx = P[r][0];
+        for (int r = 0; r < R; ++r) {
+            mx[r] = P[r][0];
 #pragma unroll
-        for (int c = 1; c < CW; ++c) mx = fmaxf(mx, P[r][c]);
-        mx = row_allreduce<M, true>(mx);
-        float e[CW];
+            for (int c = 1; c < CW; ++c) mx[r] = fmaxf(mx[r], P[r][c]);
+        }
+        row_allreduce_slots<M, true>(mx);
 #pragma unroll
-        for (int c = 0; c < CW; ++c) e[c] = ex2(P[r][c] - mx);
-        const float a = log2N - mx - lg2(row_allreduce<M, false>(tree_sum<CW>(e)));
+        for (int r = 0; r < R; ++r) {
+            float e[CW];
 #pragma unroll
-        for (int c = 0; c < CW; ++c) P[r][c] += a;
+            for (int c = 0; c < CW; ++c) e[c] = ex2(P[r][c] - mx[r]);
+            sm[r] = tree_sum<CW>(e);
+        }
+        row_allreduce_slots<M, false>(sm);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float a = log2N - mx[r] - lg2(sm[r]);
+#pragma unroll
+            for (int c = 0; c < CW; ++c) P[r][c] += a;
+        }
     }
     {  // C2: column max, then column sum of 2^(x - max)
         float part[CW], cmax[CW], csum[CW];
@@ -422,7 +446,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             col_reduce_scatter<true>(cmax);
             col_all_gather(cmax);
         } else if constexpr (L > 1) {
-            col_exchange<M, 0, true>(part, cmax, lds, blk, lb, fN, false);
+            col_exchange<M, 0, true>(part, cmax, lds, blk, lb, false);
         } else {
 #pragma unroll
             for (int c = 0; c < CW; ++c) cmax[c] = part[c];
@@ -440,7 +464,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             col_reduce_scatter<false>(csum);
             col_all_gather(csum);
         } else if constexpr (L > 1) {
-            col_exchange<M, 0, false>(part, csum, lds, blk, lb, fN, false);
+            col_exchange<M, 0, false>(part, csum, lds, blk, lb, false);
         } else {
 #pragma unroll
             for (int c = 0; c < CW; ++c) csum[c] = part[c];
@@ -489,28 +513,65 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         for (int c = 0; c < kCPL<M>; ++c) bcr[lb * kCPL<M> + c] = 1.f;
         // made visible by the first exchange's barrier
     }
+    // Per cycle: row r's total s_r gives the row factor a_r = N / s_r (U_r <-
+    // U_r a_r) and the column totals of E a_r give the column factors.  With
+    // H = 1 the factor enters as (U_r N) (1 / s_r) and the column totals as
+    // sums of E / s_r, i.e. divided by N, so that each column factor is one
+    // reciprocal (V <- V / cacc); the M = 32 tile keeps a_r = N (1 / s_r),
+    // which measured faster there.
     for (int it = 1; it < prm.iters; ++it) {
         float cacc[CW];
+        if constexpr (H == 1) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            float e[CW], acc[4];
+            for (int r = 0; r < R; ++r) {
+                float e[CW], acc[4];
 #pragma unroll
-            for (int c = 0; c < CW; ++c) {
-                // E = min(P V U, 1): the clamp folds into the second multiply
-                e[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
-                acc[c & 3] = (c < 4) ? e[c] : acc[c & 3] + e[c];
+                for (int c = 0; c < CW; ++c) {
+                    // E = min(P V U, 1): the clamp folds into the second multiply
+                    e[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
+                    acc[c & 3] = (c < 4) ? e[c] : acc[c & 3] + e[c];
+                }
+                const float a = rcpf((acc[0] + acc[1]) + (acc[2] + acc[3]));
+                U[r] = (U[r] * fN) * a;
+#pragma unroll
+                for (int c = 0; c < CW; ++c) cacc[c] = (r == 0) ? e[c] * a : fmaf(e[c], a, cacc[c]);
+                // Keep one row's temporaries live at a time: left alone, the
+                // instruction selector hoists every row's products and spills
+                // the tile.  The empty asm claims to update cacc and V, so this
+                // row's column updates complete before, and the next row's
+                // products start after, this point.  No instruction is emitted.
+                order_fence<CW>(cacc, V);
             }
-            const float rs = row_allreduce<M, false>((acc[0] + acc[1]) + (acc[2] + acc[3]));
-            const float a = fN * rcpf(rs);
-            U[r] *= a;
+        } else {
+            // Two slots at a time (see rsw): slot r here and slot r + 1 of the
+            // partner lane hold the same row, so the row total of slot r is one
+            // exchange away, and the factor of slot r + 1 is the partner's.
 #pragma unroll
-            for (int c = 0; c < CW; ++c) cacc[c] = (r == 0) ? e[c] * a : fmaf(e[c], a, cacc[c]);
-            // Keep one row's temporaries live at a time: left alone, the
-            // instruction selector hoists every row's products and spills the
-            // tile.  The empty asm claims to update cacc and V, so this row's
-            // column updates complete before, and the next row's products
-            // start after, this point.  No instruction is emitted.
-            order_fence<CW>(cacc, V);
+            for (int r = 0; r < R; r += 2) {
+                float e0[CW], e1[CW], acc0[4], acc1[4];
+#pragma unroll
+                for (int c = 0; c < CW; ++c) {
+                    e0[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
+                    acc0[c & 3] = (c < 4) ? e0[c] : acc0[c & 3] + e0[c];
+                }
+#pragma unroll
+                for (int c = 0; c < CW; ++c) {
+                    e1[c] = __builtin_amdgcn_fmed3f((P[r + 1][c] * V[c]) * U[r + 1], 0.0f, 1.0f);
+                    acc1[c & 3] = (c < 4) ? e1[c] : acc1[c & 3] + e1[c];
+                }
+                const float rs = ((acc0[0] + acc0[1]) + (acc0[2] + acc0[3])) +
+                                 dpp_mov<Lanes32::kRow>((acc1[0] + acc1[1]) + (acc1[2] + acc1[3]));
+                const float a0 = fN * rcpf(rs);
+                const float a1 = dpp_mov<Lanes32::kRow>(a0);
+                U[r] *= a0;
+                U[r + 1] *= a1;
+#pragma unroll
+                for (int c = 0; c < CW; ++c) {
+                    cacc[c] = (r == 0) ? e0[c] * a0 : fmaf(e0[c], a0, cacc[c]);
+                    cacc[c] = fmaf(e1[c], a1, cacc[c]);
+                }
+                order_fence<CW>(cacc, V);  // as above, per pair of slots
+            }
         }
         // Scale guard.  After cycle 1 every row/column factor lies in
         // [1/M, M], so checking every 4th cycle against 2^+-40 keeps P V U,
@@ -518,7 +579,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         bool bad = false;
         if constexpr (L == 1) {
 #pragma unroll
-            for (int c = 0; c < CW; ++c) V[c] = V[c] * (fN * rcpf(cacc[c]));
+            for (int c = 0; c < CW; ++c) V[c] = V[c] * rcpf(cacc[c]);
             if ((it & 3) == 0) {
                 float lo = V[0], hi = V[0];
 #pragma unroll
@@ -537,7 +598,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             }
             col_all_gather(V);
         } else {
-            bad = col_exchange<M, 1, false>(cacc, V, lds, blk, lb, fN, (it & 3) == 0);
+            bad = col_exchange<M, 1, false>(cacc, V, lds, blk, lb, (it & 3) == 0);
         }
         if ((it & 3) != 0) continue;
 #pragma unroll
@@ -605,13 +666,13 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         float s[CW];
 #pragma unroll
         for (int c = 0; c < CW; ++c) s[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
-        float* srow = slot + blk * M * M + (g * R + r) * M + h * CW;
+        float* srow = slot + blk * M * M + (g * R + (r ^ rsw)) * M + h * CW;
 #pragma unroll
         for (int q = 0; q < CW / 4; ++q)
             *reinterpret_cast<float4*>(srow + 4 * (q ^ sw)) =
                 make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
         if (job.frac != nullptr && valid) {
-            float* frow = job.frac + (row0 + r) * job.cols + col0;
+            float* frow = job.frac + (row0 + (r ^ rsw)) * job.cols + col0;
             if (fvec) {
 #pragma unroll
                 for (int q = 0; q < CW / 4; ++q)
