@@ -40,8 +40,8 @@ KERNEL_SOURCE = os.path.join(ROOT, "sparse_mask_search_amd", "csrc", "tsenor_ker
 # they were taken on.
 TRAFFIC = {
     "16:32-8192x28672-bf16": {
-        "kernel_sha256": "09aec0913e5e57e698b7e6185b2320e6f68eae175866a252e1e23fab0b9790b9",
-        "read_bytes": 866349.53125 * 1024 * 2.0, "write_bytes": 964848.625 * 1024 * 1.0},
+        "kernel_sha256": "8aaf5bb0e1579b69065160598092e0de3b7bc953ab43d5d149c4c9abce33a09b",
+        "read_bytes": 896894.875 * 1024 * 2.0, "write_bytes": 966416.125 * 1024 * 1.0},
 }
 
 
