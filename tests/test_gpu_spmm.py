@@ -52,7 +52,12 @@ def test_overfull_groups_counted_on_gpu():
     assert np.array_equal(meta.cpu().numpy().view(np.uint32), m0)
 
 
-@pytest.mark.parametrize("n,rows,cols", [(128, 256, 384), (256, 512, 256), (512, 768, 1408)])
+# The last two shapes give tile grids (m-tiles x n-tiles) whose workgroups are
+# spread over the 8 XCDs in groups of up to 8 m-tiles: 10 x 4 tiles of 256 and
+# 9 x 8 tiles of 128 in the forward product (ragged last groups), 1 x 8 tiles
+# of 128 in both data-gradient products.
+@pytest.mark.parametrize("n,rows,cols", [(128, 256, 384), (256, 512, 256), (512, 768, 1408),
+                                         (1024, 2560, 128), (1024, 1152, 128)])
 def test_forward_and_data_gradient(n, rows, cols):
     import torch
     print(f"[case] spmm n={n} W {rows}x{cols}", flush=True)
