@@ -102,12 +102,12 @@ static_assert(kWave * kR<32> * kCW<32> <= kSlotFloats && kWave * kR<16> * kCW<16
 constexpr float kDeepLog2 = -100.0f;
 
 // LDS exchange (M = 16): partial rows of the G row groups per block, then the
-// broadcast rows of V.
+// broadcast rows of V.  M = 32 only broadcasts V there (one row per block).
 template <int M> constexpr int kRowStride = M + 4;                      // floats per partial row
 template <int M> constexpr int kBlkStride = kG<M> * kRowStride<M>;      // floats per block
 template <int M> constexpr int kBcastOff = kBPG<M> * kBlkStride<M>;     // start of V rows
 template <int M> constexpr int dyk_lds_floats() {
-    return (kL<M> == 1 || kBfly<M>) ? 0 : kBcastOff<M> + kBPG<M> * kRowStride<M>;
+    return kBfly<M> ? kBPG<M> * M : (kL<M> == 1) ? 0 : kBcastOff<M> + kBPG<M> * kRowStride<M>;
 }
 // Rounding staging: block q of a pass at q*kStageBlk, row i at i*(M+4); the
 // block stride is M (mod 32) apart so that column reads of the blocks that
@@ -588,7 +588,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             }
         } else if constexpr (kBfly<M>) {
             // column totals by butterfly; each owner rescales its 4 columns
-            // and the new scales are gathered back
+            // (column quad g of its half) and the new scales are gathered back
             col_reduce_scatter<false>(cacc);
 #pragma unroll
             for (int c = 0; c < 4; ++c) V[c] = V[c] * (fN * rcpf(cacc[c]));
@@ -596,7 +596,21 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 #pragma unroll
                 for (int c = 0; c < 4; ++c) bad |= !(V[c] >= 0x1p-40f && V[c] <= 0x1p40f);
             }
-            col_all_gather(V);
+            {
+                // The new scales reach the other lanes through LDS (one 16-byte
+                // write per owner, three reads per lane) rather than by 12 DPP
+                // moves: each DPP operation costs the SIMD far more issue time
+                // than its one slot, while LDS traffic leaves the VALU free.  A
+                // workgroup is one wave, so the barrier only orders the accesses.
+                float* vb = lds + blk * M + h * CW;
+                *reinterpret_cast<float4*>(vb + 4 * g) = make_float4(V[0], V[1], V[2], V[3]);
+                __syncthreads();
+#pragma unroll
+                for (int k = 1; k < 4; ++k) {
+                    const float4 v = *reinterpret_cast<const float4*>(vb + 4 * (k ^ sw));
+                    V[4 * k] = v.x; V[4 * k + 1] = v.y; V[4 * k + 2] = v.z; V[4 * k + 3] = v.w;
+                }
+            }
         } else {
             bad = col_exchange<M, 1, false>(cacc, V, lds, blk, lb, (it & 3) == 0);
         }
