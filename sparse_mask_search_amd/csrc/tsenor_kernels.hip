@@ -65,33 +65,35 @@ template <int M> constexpr int kCW = M / kH<M>;         // columns per lane
 template <int M> constexpr int kG = M / kR<M>;           // row groups per block
 template <int M> constexpr int kL = kG<M> * kH<M>;       // lanes per block
 template <int M> constexpr int kBPG = kWave / kL<M>;     // blocks per group
-template <int M> constexpr int kCPL = M / kL<M>;         // columns finalised per lane
 static_assert(kBPG<32> * 32 % 32 == 0 && kBPG<16> * 16 % 32 == 0, "groups cover whole words");
 
-// Column sums of blocks spread over several lanes (M = 16 and 32) meet in
-// one of two ways, whichever measured faster for the tile shape:
-//  * M = 16 (4 lanes per block, one row group each): partial sums go through
-//    LDS -- reduce-scatter, then a broadcast of the new column scales.
-//  * M = 32 (8 lanes per block, 4 row groups x 2 row halves): a DPP
-//    butterfly in registers.  Every cross-lane step is then one DPP move
-//    inside an aligned group of 8 lanes: the two halves of a row pair up by
-//    one pattern, and the 4 row groups by two further patterns g1, g0 that
-//    commute with it.  Block lane lb = bits (b2 b1 b0): g1 = b2, g0 = b0^b2,
-//    h = b1^b2; row halves pair as lane^2 (quad_perm [2,3,0,1]), g1 as
-//    lane^7 (row_half_mirror), g0 as lane^1.  Row group g = 2*g1 + g0 holds
-//    rows g*R .. g*R+R-1, and its CW = 16 columns are stored with the
-//    4-column quads permuted: register quad k holds column quad k ^ g.  Two
-//    lanes that differ only in g1 then hold each other's register quads 0-1
-//    in their quads 2-3, and lanes that differ only in g0 hold each other's
-//    quad 0 in quad 1, so the reduce-scatter of the column sums and the
-//    all-gather of the new scales are uniform DPP operations.
-template <int M> constexpr bool kBfly = (M == 32);
+// Column sums of blocks spread over several lanes (M = 16: 4 lanes per block,
+// one row group each; M = 32: 8 lanes per block, 4 row groups x 2 row halves)
+// meet by a DPP butterfly in registers (reduce-scatter: each lane ends up
+// owning 4 columns), and the owners' new column scales go back to every lane
+// through LDS.  Every cross-lane step of the butterfly is one DPP move inside
+// an aligned group of 4 or 8 lanes.  M = 32: the two halves of a row pair up
+// by one pattern, and the 4 row groups by two further patterns g1, g0 that
+// commute with it.  Block lane lb = bits (b2 b1 b0): g1 = b2, g0 = b0^b2,
+// h = b1^b2; row halves pair as lane^2 (quad_perm [2,3,0,1]), g1 as lane^7
+// (row_half_mirror), g0 as lane^1.  M = 16: g = lb, so g1 = b1 pairs as
+// lane^2 and g0 = b0 as lane^1.  Row group g = 2*g1 + g0 holds rows g*R ..
+// g*R+R-1, and its CW = 16 columns are stored with the 4-column quads
+// permuted: register quad k holds column quad k ^ g.  Two lanes that differ
+// only in g1 then hold each other's register quads 0-1 in their quads 2-3,
+// and lanes that differ only in g0 hold each other's quad 0 in quad 1, so the
+// reduce-scatter of the column sums, and in cycle 1 the all-gather of the
+// column maxima and sums, are uniform DPP operations.
+template <int M> constexpr bool kBfly = (M == 32 || M == 16);
 struct Lanes32 {
     static constexpr int kRow = 0x4E, kG1 = 0x141, kG0 = 0xB1;
     __device__ static int g(int lb) { return 2 * (lb >> 2) + ((lb ^ (lb >> 2)) & 1); }
     __device__ static int h(int lb) { return ((lb >> 1) ^ (lb >> 2)) & 1; }
 };
+template <int M> constexpr int kCtlG1 = (M == 32) ? Lanes32::kG1 : 0x4E;
+template <int M> constexpr int kCtlG0 = Lanes32::kG0;
 static_assert(kCW<32> == 16 && kG<32> == 4 && kH<32> == 2, "the butterfly's tile shape");
+static_assert(kCW<16> == 16 && kG<16> == 4 && kH<16> == 1, "the butterfly's tile shape");
 static_assert(kWave * kR<32> * kCW<32> <= kSlotFloats && kWave * kR<16> * kCW<16> <= kSlotFloats &&
                   kWave * kR<8> * kCW<8> <= kSlotFloats && kWave * kR<4> * kCW<4> <= kSlotFloats,
               "every lane's log2 kernel fits the workgroup's slot");
@@ -101,14 +103,10 @@ static_assert(kWave * kR<32> * kCW<32> <= kSlotFloats && kWave * kR<16> * kCW<16
 // beyond the normal range (-126).
 constexpr float kDeepLog2 = -100.0f;
 
-// LDS exchange (M = 16): partial rows of the G row groups per block, then the
-// broadcast rows of V.  M = 32 only broadcasts V there (one row per block).
-template <int M> constexpr int kRowStride = M + 4;                      // floats per partial row
-template <int M> constexpr int kBlkStride = kG<M> * kRowStride<M>;      // floats per block
-template <int M> constexpr int kBcastOff = kBPG<M> * kBlkStride<M>;     // start of V rows
-template <int M> constexpr int dyk_lds_floats() {
-    return kBfly<M> ? kBPG<M> * M : (kL<M> == 1) ? 0 : kBcastOff<M> + kBPG<M> * kRowStride<M>;
-}
+// The butterfly tiles broadcast each cycle's new column scales through LDS:
+// one row of M floats per block of the wave.
+template <int M> constexpr int dyk_lds_floats() { return kBfly<M> ? kBPG<M> * M : 0; }
+static_assert(kL<4> == 1 && kL<8> == 1, "blocks of one lane need no column exchange");
 // Rounding staging: block q of a pass at q*kStageBlk, row i at i*(M+4); the
 // block stride is M (mod 32) apart so that column reads of the blocks that
 // share a 32-lane half hit distinct banks.
@@ -263,77 +261,26 @@ __device__ __forceinline__ void row_allreduce_slots(float (&x)[kR<M>]) {
 // Butterfly (M = 32): on return x[0..3] of every lane hold the column totals
 // (max or sum over the 4 row groups) of those register columns; each column
 // is owned by exactly one lane of the block per row half.
-template <bool MAXOP>
+template <int M, bool MAXOP>
 __device__ __forceinline__ void col_reduce_scatter(float (&x)[16]) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-        const float y = dpp_mov<Lanes32::kG1>(x[c + 8]);
+        const float y = dpp_mov<kCtlG1<M>>(x[c + 8]);
         x[c] = MAXOP ? fmaxf(x[c], y) : x[c] + y;
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const float y = dpp_mov<Lanes32::kG0>(x[c + 4]);
+        const float y = dpp_mov<kCtlG0<M>>(x[c + 4]);
         x[c] = MAXOP ? fmaxf(x[c], y) : x[c] + y;
     }
 }
 // Inverse: from the owners' x[0..3], every lane gets x[0..15] for its columns.
+template <int M>
 __device__ __forceinline__ void col_all_gather(float (&x)[16]) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) x[c + 4] = dpp_mov<Lanes32::kG0>(x[c]);
+    for (int c = 0; c < 4; ++c) x[c + 4] = dpp_mov<kCtlG0<M>>(x[c]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) x[c + 8] = dpp_mov<Lanes32::kG1>(x[c]);
-}
-
-// Column totals of a block whose rows are spread over G row groups: lane
-// (g, h) writes its CW partials to row g, columns [h*CW, h*CW + CW); lane lb
-// of the block combines columns [lb*CPL, lb*CPL + CPL) over the G rows and
-// stores them to the block's broadcast row, from which every lane reads its
-// own CW columns.  KIND 0 broadcasts the totals (combine = max or sum);
-// KIND 1 turns each total C_j into V_j / C_j with V_j the value currently in
-// the broadcast row (the cycle loop's column totals carry a factor 1/N, see
-// there) and, when `check` is set, returns whether any new V_j of this lane
-// left [2^-40, 2^40].
-template <int M, int KIND, bool MAXOP>
-__device__ __forceinline__ bool col_exchange(const float (&part)[kCW<M>], float (&out)[kCW<M>],
-                                             float* lds, int blk, int lb, bool check) {
-    constexpr int CW = kCW<M>, G = kG<M>, H = kH<M>, CPL = kCPL<M>;
-    const int g = lb / H, h = lb % H;
-    float* mine = lds + blk * kBlkStride<M> + g * kRowStride<M> + h * CW;
-#pragma unroll
-    for (int q = 0; q < CW / 4; ++q)
-        *reinterpret_cast<float4*>(mine + 4 * q) =
-            make_float4(part[4 * q], part[4 * q + 1], part[4 * q + 2], part[4 * q + 3]);
-    __syncthreads();
-    const float* base = lds + blk * kBlkStride<M> + lb * CPL;
-    float acc[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = base[c];
-#pragma unroll
-    for (int gg = 1; gg < G; ++gg)
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const float v = base[gg * kRowStride<M> + c];
-            acc[c] = MAXOP ? fmaxf(acc[c], v) : acc[c] + v;
-        }
-    float* bc = lds + kBcastOff<M> + blk * kRowStride<M>;
-    bool bad = false;
-    if constexpr (KIND == 1) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] = bc[lb * CPL + c] * rcpf(acc[c]);
-        if (check) {
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) bad |= !(acc[c] >= 0x1p-40f && acc[c] <= 0x1p40f);
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) bc[lb * CPL + c] = acc[c];
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < CW / 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(bc + h * CW + 4 * q);
-        out[4 * q] = v.x; out[4 * q + 1] = v.y; out[4 * q + 2] = v.z; out[4 * q + 3] = v.w;
-    }
-    return bad;
+    for (int c = 0; c < 8; ++c) x[c + 8] = dpp_mov<kCtlG1<M>>(x[c]);
 }
 
 // Register-level ordering point: an empty asm that "reads and writes" a and
@@ -362,7 +309,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     if constexpr (M >= 32) asm volatile("" : "+v"(lane));
     const int blk = lane / L, lb = lane % L;
     int g = lb / H, h = lb % H;
-    if constexpr (kBfly<M>) { g = Lanes32::g(lb); h = Lanes32::h(lb); }
+    if constexpr (M == 32) { g = Lanes32::g(lb); h = Lanes32::h(lb); }
     const int sw = kBfly<M> ? g : 0;  // register quad k holds column quad k ^ sw
     // Slot k of the lane's tile holds tile row k ^ rsw: the two lanes of a
     // tile row (H = 2) hold each pair of rows in opposite slot order, so one
@@ -443,10 +390,8 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         if constexpr (kBfly<M>) {
 #pragma unroll
             for (int c = 0; c < CW; ++c) cmax[c] = part[c];
-            col_reduce_scatter<true>(cmax);
-            col_all_gather(cmax);
-        } else if constexpr (L > 1) {
-            col_exchange<M, 0, true>(part, cmax, lds, blk, lb, false);
+            col_reduce_scatter<M, true>(cmax);
+            col_all_gather<M>(cmax);
         } else {
 #pragma unroll
             for (int c = 0; c < CW; ++c) cmax[c] = part[c];
@@ -461,10 +406,8 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         if constexpr (kBfly<M>) {
 #pragma unroll
             for (int c = 0; c < CW; ++c) csum[c] = part[c];
-            col_reduce_scatter<false>(csum);
-            col_all_gather(csum);
-        } else if constexpr (L > 1) {
-            col_exchange<M, 0, false>(part, csum, lds, blk, lb, false);
+            col_reduce_scatter<M, false>(csum);
+            col_all_gather<M>(csum);
         } else {
 #pragma unroll
             for (int c = 0; c < CW; ++c) csum[c] = part[c];
@@ -507,12 +450,6 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     for (int c = 0; c < CW; ++c) V[c] = 1.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) U[r] = 1.f;
-    if constexpr (!kBfly<M> && L > 1) {
-        float* bcr = lds + kBcastOff<M> + blk * kRowStride<M>;
-#pragma unroll
-        for (int c = 0; c < kCPL<M>; ++c) bcr[lb * kCPL<M> + c] = 1.f;
-        // made visible by the first exchange's barrier
-    }
     // Per cycle: row r's total s_r gives the row factor a_r = N / s_r (U_r <-
     // U_r a_r) and the column totals of E a_r give the column factors.  With
     // H = 1 the factor enters as (U_r N) (1 / s_r) and the column totals as
@@ -586,12 +523,16 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                 for (int c = 1; c < CW; ++c) { lo = fminf(lo, V[c]); hi = fmaxf(hi, V[c]); }
                 bad = !(lo >= 0x1p-40f && hi <= 0x1p40f);
             }
-        } else if constexpr (kBfly<M>) {
+        } else {
+            static_assert(kBfly<M>, "blocks of several lanes use the butterfly");
             // column totals by butterfly; each owner rescales its 4 columns
             // (column quad g of its half) and the new scales are gathered back
-            col_reduce_scatter<false>(cacc);
+            col_reduce_scatter<M, false>(cacc);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) V[c] = V[c] * (fN * rcpf(cacc[c]));
+            for (int c = 0; c < 4; ++c) {
+                if constexpr (H == 1) V[c] = V[c] * rcpf(cacc[c]);
+                else V[c] = V[c] * (fN * rcpf(cacc[c]));
+            }
             if ((it & 3) == 0) {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) bad |= !(V[c] >= 0x1p-40f && V[c] <= 0x1p40f);
@@ -611,8 +552,6 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                     V[4 * k] = v.x; V[4 * k + 1] = v.y; V[4 * k + 2] = v.z; V[4 * k + 3] = v.w;
                 }
             }
-        } else {
-            bad = col_exchange<M, 1, false>(cacc, V, lds, blk, lb, (it & 3) == 0);
         }
         if ((it & 3) != 0) continue;
 #pragma unroll
@@ -660,15 +599,6 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                 for (int c = 0; c < CW; ++c) V[c] = 1.f;
 #pragma unroll
                 for (int r = 0; r < R; ++r) U[r] = 1.f;
-            }
-            if constexpr (!kBfly<M> && L > 1) {
-                float* bcr = lds + kBcastOff<M> + blk * kRowStride<M>;
-                __syncthreads();
-                if (f) {
-#pragma unroll
-                    for (int c = 0; c < kCPL<M>; ++c) bcr[lb * kCPL<M> + c] = 1.f;
-                }
-                __syncthreads();
             }
         }
     }
