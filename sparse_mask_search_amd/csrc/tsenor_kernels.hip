@@ -24,8 +24,8 @@
 //              output modifier (the clip), add, fma -- and no transcendental
 //              per element.  Rows live in lanes; the column sums of blocks
 //              spread over several lanes meet in a DPP butterfly
-//              (reduce-scatter, per-owner update of V, all-gather), so the
-//              solve touches no LDS.
+//              (reduce-scatter, per-owner update of V), and the owners' new
+//              V goes back to every lane through LDS.
 //  3. export   S = min(P V U, 1) is written to the workgroup's scratch slot
 //              (and to frac_out when asked).
 //  4. round    blocks are re-read from the slot one row and one column per
@@ -52,8 +52,8 @@ namespace {
 
 // Solve layout: each lane holds an R x CW tile (R rows, CW = M/H columns) of
 // one block, a block spans L = (M/R)*H lanes and a group is BPG = 64/L
-// blocks.  Row sums are completed across the H lanes of a row group, column
-// sums across the G = M/R row groups, both by DPP moves.
+// blocks.  Row sums are completed across the H lanes of a row group by DPP
+// moves, column sums across the G = M/R row groups by a DPP reduce-scatter.
 template <int M> struct Geo;
 template <> struct Geo<4> { static constexpr int R = 4, H = 1; };
 template <> struct Geo<8> { static constexpr int R = 8, H = 1; };
