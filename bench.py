@@ -224,7 +224,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the method has no "
-              "cross-GPU step and this build measures a single MI355X.", file=sys.stderr)
+              "cross-GPU step, and the benchmark measures a single MI355X.", file=sys.stderr)
         sys.exit(2)
 
     if args.workload == MODEL7B:
