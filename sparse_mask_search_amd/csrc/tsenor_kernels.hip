@@ -294,6 +294,21 @@ __device__ __forceinline__ void order_fence(float (&a)[CW], float (&b)[CW]) {
                           "+v"(b[c]), "+v"(b[c + 1]), "+v"(b[c + 2]), "+v"(b[c + 3]));
 }
 
+// Orders this wave's LDS accesses at a point, for the compiler only.  Every
+// kernel in this file runs one-wave workgroups, and a wave's LDS instructions
+// execute in issue order, so a read issued after a write (by any lane of the
+// wave) observes it with no barrier and no wait; the empty asm keeps the
+// compiler from moving LDS accesses across the point.  Global memory is still
+// ordered by __syncthreads().
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("" ::: "memory"); }
+// The rounding's LDS ordering points: the wave-level fence for M <= 8, a
+// workgroup barrier for M >= 16 (each measured the faster of the two there).
+template <int M>
+__device__ __forceinline__ void rnd_sync() {
+    if constexpr (M <= 8) wave_lds_fence();
+    else __syncthreads();
+}
+
 // ---------------------------------------------------------------- solve
 // Dykstra for the group's blocks; writes S (fp32) for block b of the group to
 // slot[b*M*M ...] row-major, and to job.frac when requested.
@@ -541,11 +556,10 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                 // The new scales reach the other lanes through LDS (one 16-byte
                 // write per owner, three reads per lane) rather than by 12 DPP
                 // moves: each DPP operation costs the SIMD far more issue time
-                // than its one slot, while LDS traffic leaves the VALU free.  A
-                // workgroup is one wave, so the barrier only orders the accesses.
+                // than its one slot, while LDS traffic leaves the VALU free.
                 float* vb = lds + blk * M + h * CW;
                 *reinterpret_cast<float4*>(vb + 4 * g) = make_float4(V[0], V[1], V[2], V[3]);
-                __syncthreads();
+                wave_lds_fence();
 #pragma unroll
                 for (int k = 1; k < 4; ++k) {
                     const float4 v = *reinterpret_cast<const float4*>(vb + 4 * (k ^ sw));
@@ -879,7 +893,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
 #pragma unroll
         for (int j = 0; j < M; ++j) Ai[j] = a[j];
     }
-    __syncthreads();
+    rnd_sync<M>();
     uint32_t rpb[M], cpb[M];
     // An opaque zero in the keys' low words: with compile-time constants there
     // the scheduler interleaves both sorts and runs out of registers.
@@ -929,7 +943,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     if (__ballot(need) != 0ull) {
         const float* Ai = As + (q * M + i) * (M + 1);
         Zs[q * M + i] = Z;
-        __syncthreads();
+        rnd_sync<M>();
 
         int moves = 0;
         bool active = need && ls_steps > 0;
@@ -962,7 +976,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
                     }
                 }
                 best = group_max_u64<M>(best);
-                __syncthreads();
+                rnd_sync<M>();
                 if (active) {
                     const float sc = ord_to_float((uint32_t)(best >> 32));
                     if (best == 0ull || !(sc > 0.f)) {
@@ -980,7 +994,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
                         if (D == 0 || moves >= ls_steps) active = false;
                     }
                 }
-                __syncthreads();
+                rnd_sync<M>();
                 DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
                 DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
             }
@@ -1014,7 +1028,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
                     Cm[i] = cmax;
                 }
                 const uint32_t CM = (uint32_t)(__ballot(hc) >> shift) & FULL;
-                __syncthreads();
+                rnd_sync<M>();
                 uint32_t sk = 0u;  // ordered key of the lane's best score, 0 = no candidate
                 uint32_t J = 0u;   // the columns j' attaining it
                 if (active && hr) {
@@ -1080,7 +1094,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
                 const uint32_t IP = (uint32_t)(__ballot(Jf != 0u) >> shift) & FULL;
                 const int bip = IP ? __ffs(IP) - 1 : M;
                 const int bjp = (int)group_max_u32<M>(i == bip ? (uint32_t)(__ffs(Jf) - 1) : 0u);
-                __syncthreads();
+                rnd_sync<M>();
                 if (active) {
                     if (bip >= M) {
                         active = false;  // unreachable: G is attained by construction
@@ -1094,7 +1108,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
                         if (D == 0 || moves >= ls_steps) active = false;
                     }
                 }
-                __syncthreads();
+                rnd_sync<M>();
                 DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
                 DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
             }
@@ -1118,7 +1132,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
                 }
             }
             best = group_max_u64<M>(best);
-            __syncthreads();
+            rnd_sync<M>();
             if (active) {
                 if (best == 0ull) {
                     active = false;  // unreachable while the invariant holds
@@ -1134,7 +1148,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
                     if (D == 0) active = false;
                 }
             }
-            __syncthreads();
+            rnd_sync<M>();
             DR = (uint32_t)(__ballot(r < N) >> shift) & FULL;
             DC = (uint32_t)(__ballot(c < N) >> shift) & FULL;
         }
