@@ -108,8 +108,9 @@ int tsenor_mask(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld
  *            strictly more score, sum over rows i ascending of the row sums
  *            over j ascending of |W_ij|, both in fp64; so the result is never
  *            worse than the previous mask.  Blocks where the previous mask is
- *            not feasible ignore it.  prev_mask may alias mask_out (in-place
- *            update).
+ *            not feasible ignore it.  prev_mask may alias or overlap mask_out
+ *            (in-place update): an overlapping previous mask is copied to a
+ *            cached device buffer before the solve writes mask_out.
  * Other arguments, errors and conventions as in tsenor_mask (polish_steps < 0
  * is TSENOR_ERR_PARAM).  tsenor_mask(...) equals tsenor_mask_ex(..., 0, NULL, ...). */
 int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,
@@ -184,17 +185,22 @@ typedef struct {
  * transformer.  `mats` is a HOST array of `count` descriptors (count >= 0; 0
  * is a no-op); every descriptor is validated as in tsenor_mask before
  * anything is enqueued.  tau, iters and ls_steps apply to all matrices.  The
- * descriptor table is copied to the device on `stream` before the call
- * returns, so `mats` may be reused immediately.  Each matrix's mask and S
- * are those tsenor_mask gives for it alone.                                  */
+ * descriptor table is built in one of eight pinned host staging buffers
+ * (used in turn) and uploaded on `stream`, so `mats` may be reused as soon
+ * as the call returns.  The call does not wait for the device, except when
+ * the staging buffer it takes still holds the table of the batched call
+ * eight calls earlier whose upload has not yet run.  Each matrix's mask and
+ * S are those tsenor_mask gives for it alone.                                */
 int tsenor_mask_batched(const tsenor_matrix* mats, int count, float tau, int iters,
                         int ls_steps, void* stream);
 
 /* tsenor_mask_batched with tsenor_mask_ex's optional stages for every matrix:
  * polish_steps >= 0 as in tsenor_mask_ex; prev_masks is NULL or a HOST array
  * of `count` device pointers, entry i a previous mask for matrix i (layout of
- * its mask_out; may alias that mask_out) or NULL.  Each matrix's result equals
- * tsenor_mask_ex's for it alone.  polish_steps < 0 is TSENOR_ERR_PARAM.       */
+ * its mask_out) or NULL.  A previous mask may alias or overlap the mask_out of
+ * any matrix of the call: such masks are copied to a cached device buffer
+ * before any solve writes.  Each matrix's result equals tsenor_mask_ex's for
+ * it alone.  polish_steps < 0 is TSENOR_ERR_PARAM.                           */
 int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int iters,
                            int ls_steps, int polish_steps, const uint32_t* const* prev_masks,
                            void* stream);

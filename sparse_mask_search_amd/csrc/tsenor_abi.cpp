@@ -19,6 +19,7 @@
 using tsenor::MatJob;
 using tsenor::Params;
 
+
 namespace {
 
 thread_local char g_last_error[256] = "";
@@ -29,16 +30,23 @@ int hip_fail(hipError_t e, const char* where) {
 }
 
 constexpr int kMaxDevices = 64;
+// Pinned staging buffers for the batched descriptor table, used in turn: a
+// call waits on the host only while the upload from its buffer, issued
+// kStageRing calls earlier, is still queued behind unfinished work.
+constexpr int kStageRing = 8;
 
 struct DeviceState {
     std::mutex mu;
-    bool init = false;
+    bool init = false;              // num_cu and the occupancy tables
+    bool ordered = false;           // `last` exists
     int num_cu = 0;
     float* scratch = nullptr;
-    size_t scratch_slots = 0;
+    size_t scratch_floats = 0;
     hipEvent_t last = nullptr;      // completion of the newest launch that used this state
     MatJob* jobs_dev = nullptr;     // batched descriptor table (device)
-    MatJob* jobs_host = nullptr;    // pinned staging copy
+    MatJob* jobs_host[kStageRing] = {};   // pinned staging copies, used in turn
+    hipEvent_t jobs_up[kStageRing] = {};  // completion of the upload from each
+    int jobs_next = 0;
     size_t jobs_cap = 0;
     int occ_mask[2][33] = {};
     int occ_round[2][33] = {};
@@ -97,8 +105,9 @@ int64_t groups_of(const MatJob& j) {
     return (j.rows / j.M) * ((nbc + bpg - 1) / bpg);
 }
 
-// Lock, initialise and return the current device's state.
-int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
+// Lock the current device's state and fill in its launch geometry (CU count,
+// occupancy of every kernel).  Creates no HIP object and allocates nothing.
+int acquire_geometry(DeviceState** out, std::unique_lock<std::mutex>* lk) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -108,8 +117,6 @@ int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
     if (!st.init) {
         e = hipDeviceGetAttribute(&st.num_cu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-        e = hipEventCreateWithFlags(&st.last, hipEventDisableTiming);
-        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
         for (int b = 0; b < 2; ++b)
             for (int M : {4, 8, 16, 32}) {
                 st.occ_mask[b][M] = tsenor::occupancy_mask(M, b);
@@ -124,10 +131,24 @@ int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
     return TSENOR_OK;
 }
 
-// Ensure `slots` workspace slots exist.  Growing waits for every earlier
-// launch that may still read the old buffer.
-int ensure_scratch(DeviceState& st, size_t slots) {
-    if (st.scratch_slots >= slots) return TSENOR_OK;
+// acquire_geometry, plus the event that orders the launches sharing the
+// cached workspace.
+int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
+    int code = acquire_geometry(out, lk);
+    if (code != TSENOR_OK) return code;
+    DeviceState& st = **out;
+    if (!st.ordered) {
+        hipError_t e = hipEventCreateWithFlags(&st.last, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        st.ordered = true;
+    }
+    return TSENOR_OK;
+}
+
+// Ensure the workspace holds `floats` floats.  Growing waits for every
+// earlier launch that may still read the old buffer.
+int ensure_scratch(DeviceState& st, size_t floats) {
+    if (st.scratch_floats >= floats) return TSENOR_OK;
     hipError_t e;
     if (st.scratch != nullptr) {
         e = hipEventSynchronize(st.last);
@@ -135,14 +156,14 @@ int ensure_scratch(DeviceState& st, size_t slots) {
         e = hipFree(st.scratch);
         if (e != hipSuccess) return hip_fail(e, "hipFree");
         st.scratch = nullptr;
-        st.scratch_slots = 0;
+        st.scratch_floats = 0;
     }
-    e = hipMalloc(&st.scratch, slots * tsenor::kSlotFloats * sizeof(float));
+    e = hipMalloc(&st.scratch, floats * sizeof(float));
     if (e != hipSuccess) {
         st.scratch = nullptr;
         return hip_fail(e, "hipMalloc(workspace)");
     }
-    st.scratch_slots = slots;
+    st.scratch_floats = floats;
     return TSENOR_OK;
 }
 
@@ -166,6 +187,14 @@ int ensure_prev_copy(DeviceState& st, size_t words) {
     st.prev_cap = words;
     return TSENOR_OK;
 }
+
+// True when the byte ranges [a, a + an) and [b, b + bn) share a byte.
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return an > 0 && bn > 0 && x < y + bn && y < x + an;
+}
+
+size_t mask_words(int64_t rows, int64_t cols) { return (size_t)rows * (size_t)((cols + 31) / 32); }
 
 int64_t clamp_grid(int64_t groups, int num_cu, int occ) {
     int64_t cap = (int64_t)num_cu * (occ > 0 ? occ : 1);
@@ -250,7 +279,8 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
     MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, frac_out);
     job.prev = prev_mask;
     const int64_t grid = clamp_grid(groups_of(job), st->num_cu, st->occ_mask[job.bf16][M]);
-    if ((st_code = ensure_scratch(*st, (size_t)grid)) != TSENOR_OK) return st_code;
+    if ((st_code = ensure_scratch(*st, (size_t)grid * (size_t)tsenor::slot_floats(M))) != TSENOR_OK)
+        return st_code;
     Params prm;
     prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
     prm.iters = iters;
@@ -258,13 +288,14 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
     prm.scratch = st->scratch;
     const bool refine = polish_steps > 0 || prev_mask != nullptr;
     const size_t words = (size_t)rows * (size_t)job.wpr;
-    // a previous mask that the solve overwrites is copied first
-    if (prev_mask != nullptr && prev_mask == mask_out &&
-        (st_code = ensure_prev_copy(*st, words)) != TSENOR_OK)
-        return st_code;
+    // a previous mask that the solve overwrites (any overlap with the output)
+    // is copied first
+    const bool prev_alias = prev_mask != nullptr &&
+                            overlaps(prev_mask, words * 4, mask_out, words * 4);
+    if (prev_alias && (st_code = ensure_prev_copy(*st, words)) != TSENOR_OK) return st_code;
     if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
     hipError_t e;
-    if (prev_mask != nullptr && prev_mask == mask_out) {
+    if (prev_alias) {
         e = hipMemcpyAsync(st->prev_copy, prev_mask, words * sizeof(uint32_t),
                            hipMemcpyDeviceToDevice, s);
         if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(previous mask)");
@@ -407,32 +438,49 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
         }
     hipError_t e;
     if (st->jobs_cap < (size_t)count) {
+        // Growing (rare): wait for every launch that may read the device table
+        // and every upload that may read a staging buffer, then reallocate.
         if (st->jobs_dev != nullptr) {
             e = hipEventSynchronize(st->last);
             if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
             (void)hipFree(st->jobs_dev);
-            (void)hipHostFree(st->jobs_host);
             st->jobs_dev = nullptr;
-            st->jobs_host = nullptr;
-            st->jobs_cap = 0;
         }
+        for (int k = 0; k < kStageRing; ++k) {
+            if (st->jobs_up[k] != nullptr) {
+                e = hipEventSynchronize(st->jobs_up[k]);
+                if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+            } else {
+                e = hipEventCreateWithFlags(&st->jobs_up[k], hipEventDisableTiming);
+                if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+            }
+            if (st->jobs_host[k] != nullptr) (void)hipHostFree(st->jobs_host[k]);
+            st->jobs_host[k] = nullptr;
+        }
+        st->jobs_cap = 0;
         e = hipMalloc(&st->jobs_dev, sizeof(MatJob) * (size_t)count);
         if (e != hipSuccess) return hip_fail(e, "hipMalloc(descriptors)");
-        e = hipHostMalloc(reinterpret_cast<void**>(&st->jobs_host), sizeof(MatJob) * (size_t)count,
-                          hipHostMallocDefault);
-        if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(descriptors)");
+        for (int k = 0; k < kStageRing; ++k) {
+            e = hipHostMalloc(reinterpret_cast<void**>(&st->jobs_host[k]),
+                              sizeof(MatJob) * (size_t)count, hipHostMallocDefault);
+            if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(descriptors)");
+        }
         st->jobs_cap = (size_t)count;
-    } else {
-        // the pinned staging copy may still be read by the previous upload
-        e = hipEventSynchronize(st->last);
-        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
     }
+    // This call's staging buffer: free once the upload that last read it has
+    // run (normally long ago; the host blocks only when kStageRing batched
+    // calls are queued behind unfinished work).
+    const int ring = st->jobs_next;
+    st->jobs_next = (ring + 1) % kStageRing;
+    e = hipEventSynchronize(st->jobs_up[ring]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
+    MatJob* const table = st->jobs_host[ring];
     // One launch per (M, dtype) class present; the class's descriptors are
     // contiguous in the table, in call order, with group ids counted from 0.
     struct Class { int M, bf16, first, n; int64_t groups, grid; };
     Class cls[8];
     int ncls = 0, filled = 0;
-    int64_t max_grid = 0;
+    int64_t max_floats = 0;
     for (int M : {32, 16, 8, 4})
         for (int b = 0; b < 2; ++b) {
             Class c{M, b, filled, 0, 0, 0};
@@ -443,21 +491,30 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
                                     m.frac_out);
                 j.group_begin = c.groups;
                 c.groups += groups_of(j);
-                st->jobs_host[filled++] = j;
+                table[filled++] = j;
                 ++c.n;
             }
             if (c.n == 0) continue;
             c.grid = clamp_grid(c.groups, st->num_cu, st->occ_batched[b][M]);
-            max_grid = c.grid > max_grid ? c.grid : max_grid;
+            const int64_t need = c.grid * tsenor::slot_floats(M);
+            max_floats = need > max_floats ? need : max_floats;
             cls[ncls++] = c;
         }
-    if ((st_code = ensure_scratch(*st, (size_t)max_grid)) != TSENOR_OK) return st_code;
-    // previous masks that the solve overwrites are copied first, back to back
+    if ((st_code = ensure_scratch(*st, (size_t)max_floats)) != TSENOR_OK) return st_code;
+    // previous masks that any of the call's outputs overlaps are copied first,
+    // back to back (the solve of one matrix may overwrite another's previous
+    // mask before the refine stage reads it)
     size_t alias_words = 0;
+    std::vector<char> alias(count, 0);
     if (prev_masks != nullptr)
-        for (int i = 0; i < count; ++i)
-            if (prev_masks[i] != nullptr && prev_masks[i] == mats[i].mask_out)
-                alias_words += (size_t)mats[i].rows * (size_t)((mats[i].cols + 31) / 32);
+        for (int i = 0; i < count; ++i) {
+            if (prev_masks[i] == nullptr) continue;
+            const size_t words = mask_words(mats[i].rows, mats[i].cols);
+            for (int j = 0; j < count && !alias[i]; ++j)
+                alias[i] = overlaps(prev_masks[i], words * 4, mats[j].mask_out,
+                                    mask_words(mats[j].rows, mats[j].cols) * 4);
+            if (alias[i]) alias_words += words;
+        }
     if (alias_words > 0 && (st_code = ensure_prev_copy(*st, alias_words)) != TSENOR_OK)
         return st_code;
     Params prm;
@@ -466,16 +523,18 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
     prm.ls_steps = ls_steps;
     prm.scratch = st->scratch;
     if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
-    e = hipMemcpyAsync(st->jobs_dev, st->jobs_host, sizeof(MatJob) * (size_t)count,
+    e = hipMemcpyAsync(st->jobs_dev, table, sizeof(MatJob) * (size_t)count,
                        hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
+    e = hipEventRecord(st->jobs_up[ring], s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
     std::vector<const uint32_t*> prev_eff(count, nullptr);
     if (prev_masks != nullptr) {
         size_t off = 0;
         for (int i = 0; i < count; ++i) {
             prev_eff[i] = prev_masks[i];
-            if (prev_masks[i] == nullptr || prev_masks[i] != mats[i].mask_out) continue;
-            const size_t words = (size_t)mats[i].rows * (size_t)((mats[i].cols + 31) / 32);
+            if (!alias[i]) continue;
+            const size_t words = mask_words(mats[i].rows, mats[i].cols);
             e = hipMemcpyAsync(st->prev_copy + off, prev_masks[i], words * sizeof(uint32_t),
                                hipMemcpyDeviceToDevice, s);
             if (e != hipSuccess) {

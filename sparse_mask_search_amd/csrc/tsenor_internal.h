@@ -23,17 +23,20 @@ struct Params {
     float tau_log2e;    // tau * log2(e): the Gibbs exponent in base 2
     int32_t iters;
     int32_t ls_steps;
-    float* scratch;     // one slot of kSlotFloats per workgroup
+    float* scratch;     // one slot of slot_floats(M) floats per workgroup
 };
 
 // Work decomposition: one workgroup = one wave (64 lanes) processes a "group"
 // of horizontally adjacent blocks of one block-row; see blocks_per_group().
 constexpr int kWave = 64;
-constexpr int64_t kSlotFloats = 8192;  // 32 KiB: max over M of blocks_per_group * M * M
 
 // Blocks per group of the fused kernel for pattern size M (the solve layout
 // is fixed per M in tsenor_kernels.hip).
 int blocks_per_group(int M);
+// Floats of workspace one workgroup of the fused kernels uses for pattern
+// size M: the fractional S of its group, blocks_per_group(M) * M * M (4, 16,
+// 16 and 32 KiB for M = 4, 8, 16, 32); 0 for an unsupported M.
+int64_t slot_floats(int M);
 
 // Host-side launchers (tsenor_kernels.hip).  They return a hipError_t value.
 int launch_mask(const MatJob& job, const Params& prm, int grid, void* stream);

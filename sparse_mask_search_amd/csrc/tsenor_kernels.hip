@@ -99,8 +99,10 @@ template <int M> constexpr int kSwzG1 = 0x1F | (((M == 32) ? 7 : 2) << 10);
 constexpr int kSwzG0 = 0x1F | (1 << 10);
 static_assert(kCW<32> == 16 && kG<32> == 4 && kH<32> == 2, "the butterfly's tile shape");
 static_assert(kCW<16> == 16 && kG<16> == 4 && kH<16> == 1, "the butterfly's tile shape");
-static_assert(kWave * kR<32> * kCW<32> <= kSlotFloats && kWave * kR<16> * kCW<16> <= kSlotFloats &&
-                  kWave * kR<8> * kCW<8> <= kSlotFloats && kWave * kR<4> * kCW<4> <= kSlotFloats,
+// Workspace of one workgroup: the S of its group's blocks, row-major per block.
+template <int M> constexpr int64_t kSlot = (int64_t)kBPG<M> * M * M;
+static_assert(kWave * kR<32> * kCW<32> <= kSlot<32> && kWave * kR<16> * kCW<16> <= kSlot<16> &&
+                  kWave * kR<8> * kCW<8> <= kSlot<8> && kWave * kR<4> * kCW<4> <= kSlot<4>,
               "every lane's log2 kernel fits the workgroup's slot");
 // Blocks whose cycle-1 kernel reaches below 2^kDeepLog2 rescale in log2 space.
 // fp32 emulation of the iteration against the fp64 oracle: folding in the
@@ -1693,7 +1695,7 @@ void mask_kernel(MatJob job, Params prm) {
     constexpr int BPG = kBPG<M>;
     const int64_t nbc = job.cols / M;
     const int64_t ngroups = (job.rows / M) * ((nbc + BPG - 1) / BPG);
-    float* slot = prm.scratch + (int64_t)blockIdx.x * kSlotFloats;
+    float* slot = prm.scratch + (int64_t)blockIdx.x * kSlot<M>;
     for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x)
         process_group<M, BF16>(job, prm, g, slot, lds);
 }
@@ -1724,7 +1726,7 @@ template <int M, bool BF16>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kSolveWaves<M>)))
 void batched_kernel(const MatJob* __restrict__ jobs, int count, int64_t total_groups, Params prm) {
     __shared__ __attribute__((aligned(16))) float lds[lds_floats<M>()];
-    float* slot = prm.scratch + (int64_t)blockIdx.x * kSlotFloats;
+    float* slot = prm.scratch + (int64_t)blockIdx.x * kSlot<M>;
     for (int64_t g = blockIdx.x; g < total_groups; g += gridDim.x) {
         int lo = 0, hi = count - 1;
         while (lo < hi) {
@@ -1778,10 +1780,17 @@ __global__ __launch_bounds__(256) void nonfinite_kernel(const void* __restrict__
         }                                                               \
     } while (0)
 
+int64_t slot_floats(int M) {
+    switch (M) {
+        case 4: return kSlot<4>;
+        case 8: return kSlot<8>;
+        case 16: return kSlot<16>;
+        case 32: return kSlot<32>;
+        default: return 0;
+    }
+}
+
 int blocks_per_group(int M) {
-    static_assert(kBPG<4> * 16 <= kSlotFloats && kBPG<8> * 64 <= kSlotFloats &&
-                      kBPG<16> * 256 <= kSlotFloats && kBPG<32> * 1024 <= kSlotFloats,
-                  "a group's S fits one workspace slot");
     switch (M) {
         case 4: return kBPG<4>;
         case 8: return kBPG<8>;

@@ -425,6 +425,44 @@ def test_batched_ex_equals_per_matrix_ex():
     assert kept > 0
 
 
+def test_prev_mask_overlapping_outputs():
+    """A previous mask held in memory that the call's own solves write is read
+    before it is overwritten: in a batch, inside another matrix's output
+    buffer (prev_masks[0] is mats[1].mask_out); for one matrix, as a view at
+    a row offset into the output's buffer.  Results equal those with a
+    separate copy of the previous mask."""
+    import torch
+    rng = np.random.default_rng(81)
+    M, N, rows, cols = 16, 8, 48, 64
+    tau, iters, ls, K = 25.0, 40, 6, 3
+    _note("previous masks overlapping outputs")
+    Ws = [to_device(wl.f32_to_bf16_bits((0.02 * rng.standard_t(3, (rows, cols))).astype(np.float32)))
+          for _ in range(2)]
+    # a previous mask for matrix 0 polished further than this call polishes
+    p0, _ = sms.mask(Ws[0], N, M, tau, iters, ls, polish_steps=60)
+    p0 = p0.clone()
+    out0 = torch.zeros_like(p0)
+    out1 = p0.clone()  # matrix 1's output buffer holds matrix 0's previous mask
+    sms.mask_batched([(Ws[0], N, M), (Ws[1], N, M)], tau, iters, ls, outs=[out0, out1],
+                     polish_steps=K, prev_masks=[out1, None])
+    ref0, _ = sms.mask(Ws[0], N, M, tau, iters, ls, polish_steps=K, prev_mask=p0.clone())
+    ref1, _ = sms.mask(Ws[1], N, M, tau, iters, ls, polish_steps=K)
+    plain0, _ = sms.mask(Ws[0], N, M, tau, iters, ls, polish_steps=K)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, ref0) and torch.equal(out1, ref1)
+    assert not torch.equal(ref0, plain0)  # the previous mask was taken somewhere
+    # one matrix: prev = rows h .. h+rows-1 of a buffer whose rows 0 .. rows-1
+    # are the output
+    h = rows // 3
+    buf = torch.zeros((rows + h, p0.shape[1]), dtype=torch.int32, device="cuda")
+    buf[h:] = p0
+    prev_view = buf[h:]
+    m, _ = sms.mask(Ws[0], N, M, tau, iters, ls, polish_steps=K, prev_mask=prev_view,
+                    out=buf[:rows])
+    torch.cuda.synchronize()
+    assert torch.equal(m, ref0)
+
+
 def test_output_buffers_are_checked():
     """Caller-supplied mask / frac buffers of the wrong shape, dtype or layout
     are refused before anything is enqueued."""
