@@ -118,6 +118,26 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
                    const uint32_t* prev_mask, uint32_t* mask_out, float* frac_out,
                    void* stream);
 
+/* tsenor_mask for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, result (bit-identical masks and S) and argument errors as
+ * tsenor_mask.  It calls no hipMalloc, hipFree or other allocating routine and
+ * records or waits on no event: its workspace is a fixed 64 MiB array in
+ * device memory, one copy per GPU, present from the library's first kernel
+ * launch on that GPU until the process ends.  The launch grid is capped at the
+ * array's workgroup slots (on a 256-CU MI355X every M runs its full grid), so
+ * no matrix size is beyond it.  Nothing in the array needs clearing between
+ * calls (every slot is written before it is read).  Calls of this entry point
+ * on one GPU share the array: two that overlap in time (different streams, or
+ * threads without ordering) race and give undefined results; calls on one
+ * stream are ordered.  It does not share the workspace of the other entry
+ * points, so it may overlap them.  TSENOR_DEBUG_CHECKS is ignored here (its
+ * check allocates).  The first call on a device also reads the device's
+ * launch geometry (CU count, kernel occupancies).                             */
+int tsenor_mask_noalloc(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                        int N, int M, float tau, int iters, int ls_steps, uint32_t* mask_out,
+                        float* frac_out, void* stream);
+
 /* Exact optimum of every block: the mask with N ones per row and column that
  * keeps the most |W| (the block LP is a bipartite b-matching, so its optimum
  * is integral).  Not part of the method -- the reference it is measured

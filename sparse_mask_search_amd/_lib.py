@@ -49,6 +49,8 @@ def lib():
         l.tsenor_mask_ex.argtypes = [_P, _I, _I64, _I64, _I64, _I, _I, _F, _I, _I, _I, _P, _P, _P,
                                      _P]
         l.tsenor_mask_ex.restype = _I
+        l.tsenor_mask_noalloc.argtypes = [_P, _I, _I64, _I64, _I64, _I, _I, _F, _I, _I, _P, _P, _P]
+        l.tsenor_mask_noalloc.restype = _I
         l.tsenor_exact.argtypes = [_P, _I, _I64, _I64, _I64, _I, _I, _P, _I, _P, _P, _P]
         l.tsenor_exact.restype = _I
         l.tsenor_compress24.argtypes = [_P, _I64, _I64, _I64, _P, _I, _P, _P, _P, _P]
@@ -152,6 +154,32 @@ def mask(W, N: int, M: int, tau: float, iters: int, ls_steps: int, return_frac: 
                               ctypes.c_void_p(out.data_ptr()), fp, _stream(stream))
     if st != 0:
         raise TsenorError(st, "tsenor_mask_ex")
+    return out, frac_out
+
+
+def mask_noalloc(W, N: int, M: int, tau: float, iters: int, ls_steps: int, out, frac_out=None,
+                 stream=None):
+    """tsenor_mask_noalloc: the mask of W into the caller's `out` (and S into
+    `frac_out` when given), with the library allocating nothing (its
+    workspace is a fixed device array).  Overlapping calls on one GPU race."""
+    dt = _weights(W)
+    rows, cols = W.shape
+    if out is None:
+        raise ValueError("mask_noalloc needs a caller-supplied mask buffer")
+    out = _mask_buffer(W, out)
+    if frac_out is not None:
+        torch = _torch()
+        if (frac_out.dtype != torch.float32 or frac_out.device != W.device
+                or tuple(frac_out.shape) != (rows, cols) or not frac_out.is_contiguous()):
+            raise ValueError(f"frac_out must be a contiguous float32 tensor of shape "
+                             f"{(rows, cols)} on {W.device}")
+    st = lib().tsenor_mask_noalloc(ctypes.c_void_p(W.data_ptr()), dt, rows, cols, W.stride(0), N,
+                                   M, float(tau), int(iters), int(ls_steps),
+                                   ctypes.c_void_p(out.data_ptr()),
+                                   ctypes.c_void_p(frac_out.data_ptr() if frac_out is not None else 0),
+                                   _stream(stream))
+    if st != 0:
+        raise TsenorError(st, "tsenor_mask_noalloc")
     return out, frac_out
 
 

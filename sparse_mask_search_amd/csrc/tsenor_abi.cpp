@@ -19,6 +19,14 @@
 using tsenor::MatJob;
 using tsenor::Params;
 
+// Workspace of tsenor_mask_noalloc: a fixed array in device memory, one copy
+// per GPU, for callers that cannot allocate.  Host code reaches it only
+// through the address hipGetSymbolAddress returns per device (the name
+// itself is a host-side stand-in).  16 Mi floats (64 MiB) hold one workspace
+// slot per workgroup of a full persistent grid on a 256-CU device for every M
+// (M = 8 and 32 need the most: 4096 slots of 16 KiB, 2048 of 32 KiB).
+constexpr size_t kFixedScratchFloats = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kFixedScratchFloats];
 
 namespace {
 
@@ -57,6 +65,7 @@ struct DeviceState {
     size_t prev_cap = 0;            // words
     int* dbg_count = nullptr;       // debug checks: device counter and its pinned host copy
     int* dbg_host = nullptr;
+    float* fixed_scratch = nullptr; // device address of this GPU's copy of `scratch` (below)
 };
 DeviceState g_dev[kMaxDevices];
 
@@ -317,6 +326,43 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
         }
     }
     return record_end(*st, s);
+}
+
+int tsenor_mask_noalloc(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                        int N, int M, float tau, int iters, int ls_steps, uint32_t* mask_out,
+                        float* frac_out, void* stream) {
+    int st_code = check_matrix(W, dtype, rows, cols, ld, N, M, mask_out);
+    if (st_code != TSENOR_OK) return st_code;
+    st_code = check_params(tau, iters, ls_steps);
+    if (st_code != TSENOR_OK) return st_code;
+    const size_t slot = (size_t)tsenor::slot_floats(M);
+    if (slot == 0 || slot > kFixedScratchFloats) return TSENOR_ERR_NM;
+
+    DeviceState* st = nullptr;
+    std::unique_lock<std::mutex> lk;
+    if ((st_code = acquire_geometry(&st, &lk)) != TSENOR_OK) return st_code;
+    if (st->fixed_scratch == nullptr) {
+        // once per device, with that device current: this GPU's copy of the array
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+        st->fixed_scratch = static_cast<float*>(ptr);
+    }
+    MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, frac_out);
+    // The kernel's grid is persistent (workgroups stride over the groups), so
+    // any matrix runs in any grid: the grid is the usual one, capped at the
+    // number of workgroup slots the array holds.
+    int64_t grid = clamp_grid(groups_of(job), st->num_cu, st->occ_mask[job.bf16][M]);
+    const int64_t cap = (int64_t)(kFixedScratchFloats / slot);
+    if (grid > cap) grid = cap;
+    Params prm;
+    prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
+    prm.iters = iters;
+    prm.ls_steps = ls_steps;
+    prm.scratch = st->fixed_scratch;
+    hipError_t e = (hipError_t)tsenor::launch_mask(job, prm, (int)grid, stream);
+    return e == hipSuccess ? TSENOR_OK : hip_fail(e, "mask kernel launch");
 }
 
 int tsenor_exact(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld, int N, int M,

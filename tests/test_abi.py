@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol():
     names = declared()
     assert names == ["tsenor_compress24", "tsenor_exact", "tsenor_last_error", "tsenor_mask",
                      "tsenor_mask_batched", "tsenor_mask_batched_ex", "tsenor_mask_ex",
-                     "tsenor_round", "tsenor_spmm24", "tsenor_status_str", "tsenor_version"]
+                     "tsenor_mask_noalloc", "tsenor_round", "tsenor_spmm24", "tsenor_status_str",
+                     "tsenor_version"]
     out = subprocess.check_output(["nm", "-D", "--defined-only", sms.library_path()], text=True)
     exported = set(re.findall(r"\bT (tsenor_\w+)", out))
     for n in names:
@@ -58,6 +59,24 @@ def _mask(W=FAKE, dtype=1, rows=64, cols=64, ld=64, N=2, M=4, tau=20.0, iters=10
     (dict(iters=0), PARAM), (dict(ls=-1), PARAM),
 ])
 def test_mask_rejects(kw, code):
+    assert _mask(**kw) == code
+
+
+def _noalloc(W=FAKE, dtype=1, rows=64, cols=64, ld=64, N=2, M=4, tau=20.0, iters=10, ls=4,
+             mask=FAKE, frac=None):
+    return sms.lib().tsenor_mask_noalloc(W, dtype, rows, cols, ld, N, M, tau, iters, ls, mask,
+                                         frac, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=None), NULL), (dict(mask=None), NULL), (dict(dtype=2), DTYPE),
+    (dict(M=6, N=3), NM), (dict(N=0), NM), (dict(rows=66), SHAPE), (dict(ld=60), SHAPE),
+    (dict(tau=math.nan), PARAM), (dict(iters=0), PARAM), (dict(ls=-1), PARAM),
+])
+def test_mask_noalloc_rejects(kw, code):
+    """The entry point that allocates nothing validates exactly like
+    tsenor_mask, on the host, before any HIP call."""
+    assert _noalloc(**kw) == code
     assert _mask(**kw) == code
 
 
