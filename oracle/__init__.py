@@ -51,7 +51,9 @@ def _load():
         lib.oracle_dykstra.argtypes = [_P, _I64, _I64, _I64, _I, _I, _D, _I, _P, _P, _I]
         lib.oracle_dykstra_blocks.argtypes = [_P, _I64, _I64, _I64, _I, _I, _D, _I,
                                               _P, _I64, _P, _P, _I]
-        lib.oracle_round_block.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P]
+        lib.oracle_round_block.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _P, _P]
+        lib.oracle_dykstra_blocks_f32.argtypes = [_P, _I64, _I64, _I64, _I, _I, ctypes.c_float,
+                                                  _I, _P, _I64, _P, _I]
         lib.oracle_round.argtypes = [_P, _I64, _P, _I64, _I64, _I64, _I, _I, _I, _P, _P, _I]
         lib.oracle_round_block_ex.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P]
         lib.oracle_round_ex.argtypes = [_P, _I64, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P, _P,
@@ -110,24 +112,45 @@ def dykstra_blocks(W, N: int, M: int, tau: float, iters: int, block_ids, nthread
     return S64, S32
 
 
-def round_block(S32, A, N: int, ls_steps: int, trace: bool = False):
+def round_block(S32, A, N: int, ls_steps: int, trace: bool = False, moves: bool = False):
     """Greedy + local search + fill on one block.  Returns (Z uint8 [M,M], info)
     with info = (shortfall after greedy, local-search moves, fill moves); with
     trace=True also the greedy-only mask and the fp32 score of every applied
-    move, in order."""
+    move, in order; with moves=True as well (after those) the applied moves
+    as an int array [n, 4] of (i, j, i', j'), local-search moves first."""
     S32 = np.ascontiguousarray(np.asarray(S32, dtype=np.float32))
     A = np.ascontiguousarray(np.asarray(A, dtype=np.float32))
     M = S32.shape[0]
     Z = np.zeros((M, M), np.uint8)
     Zg = np.zeros((M, M), np.uint8)
     scores = np.zeros(M * M, np.float32)
+    ijs = np.zeros((M * M, 4), np.int32)
     info = np.zeros(3, np.int32)
     _check(_load().oracle_round_block(_ptr(S32), _ptr(A), N, M, ls_steps, _ptr(Z),
-                                      _ptr(info), _ptr(Zg), _ptr(scores)), "round_block")
+                                      _ptr(info), _ptr(Zg), _ptr(scores), _ptr(ijs)),
+           "round_block")
     info = tuple(int(x) for x in info)
+    n = info[1] + info[2]
+    if trace and moves:
+        return Z, info, Zg, scores[:n].copy(), ijs[:n].copy()
     if trace:
-        return Z, info, Zg, scores[:info[1] + info[2]].copy()
+        return Z, info, Zg, scores[:n].copy()
+    if moves:
+        return Z, info, ijs[:n].copy()
     return Z, info
+
+
+def dykstra_blocks_f32(W, N: int, M: int, tau: float, iters: int, block_ids, nthreads: int = 0):
+    """The Dykstra steps in fp32 (expf/logf) on the listed blocks: the method's
+    own fp32 sensitivity.  Returns S32 [len(block_ids), M, M]."""
+    W = _f32(W)
+    rows, cols = W.shape
+    ids = np.ascontiguousarray(np.asarray(block_ids, dtype=np.int64))
+    S = np.empty((len(ids), M, M), np.float32)
+    _check(_load().oracle_dykstra_blocks_f32(_ptr(W), rows, cols, cols, N, M, float(tau), iters,
+                                             _ptr(ids), len(ids), _ptr(S), nthreads),
+           "dykstra_blocks_f32")
+    return S
 
 
 def round_matrix(S32, W, N: int, M: int, ls_steps: int, nthreads: int = 0):

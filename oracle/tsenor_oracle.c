@@ -104,6 +104,54 @@ static int dykstra_block(const float* A, int N, int M, double tau, int iters,
     return OR_OK;
 }
 
+/* The same steps in fp32 (single-precision values, expf/logf, natural log):
+ * the method's own sensitivity to fp32 arithmetic.  Comparing its S with the
+ * fp64 S above bounds how far any fp32 implementation of these steps may
+ * drift from the fp64 result for reasons that lie in the iteration itself
+ * rather than in an implementation.                                        */
+static float lse_f32(const float* x, int n, int stride) {
+    float mx = -INFINITY;
+    for (int k = 0; k < n; ++k)
+        if (x[k * stride] > mx) mx = x[k * stride];
+    float s = 0.0f;
+    for (int k = 0; k < n; ++k) s += expf(x[k * stride] - mx);
+    return mx + logf(s);
+}
+
+static int dykstra_block_f32(const float* A, int N, int M, float tau, int iters, float* X,
+                             float* Q) {
+    const int n = M * M;
+    float m = 0.0f;
+    for (int k = 0; k < n; ++k) {
+        if (!isfinite(A[k])) return OR_ERR_NONFINITE;
+        if (A[k] > m) m = A[k];
+    }
+    for (int k = 0; k < n; ++k) {
+        float what = (m > 0.0f) ? A[k] / m : 0.0f;
+        X[k] = tau * what;
+        Q[k] = 0.0f;
+    }
+    const float lnN = logf((float)N);
+    for (int t = 0; t < iters; ++t) {
+        for (int i = 0; i < M; ++i) { /* C1 */
+            float a = lnN - lse_f32(X + i * M, M, 1);
+            for (int j = 0; j < M; ++j) X[i * M + j] += a;
+        }
+        for (int j = 0; j < M; ++j) { /* C2 */
+            float b = lnN - lse_f32(X + j, M, M);
+            for (int i = 0; i < M; ++i) X[i * M + j] += b;
+        }
+        for (int k = 0; k < n; ++k) { /* C3 */
+            float y = X[k] + Q[k];
+            float x = (y < 0.0f) ? y : 0.0f;
+            Q[k] = y - x;
+            X[k] = x;
+        }
+    }
+    for (int k = 0; k < n; ++k) X[k] = expf(X[k]);
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Rounding ("What carries the argument": sort descending, greedy within the
  * row/column budgets, then a local search on the swap score).
@@ -145,10 +193,12 @@ static int invariant_I(const uint8_t* Z, const int* r, const int* c, int N, int 
     return 1;
 }
 
-/* info[0] = shortfall D after R1, info[1] = R2 moves, info[2] = R3 moves */
+/* info[0] = shortfall D after R1, info[1] = R2 moves, info[2] = R3 moves.
+ * Optional traces, in the order the moves are applied: move_scores[k] the
+ * fp32 score of move k, move_ijs[4k..4k+3] its (i, j, i', j').             */
 static int round_block(const float* S, const float* A, int N, int M, int L,
                        uint8_t* Z, int* order, int* info, uint8_t* Zgreedy,
-                       float* move_scores) {
+                       float* move_scores, int* move_ijs) {
     const int n = M * M;
     for (int k = 0; k < n; ++k) {
         if (!isfinite(S[k])) return OR_ERR_NONFINITE;
@@ -199,6 +249,12 @@ static int round_block(const float* S, const float* A, int N, int M, int L,
         }
         if (!found || !(best > 0.0f)) break;
         if (move_scores) move_scores[moves] = best;
+        if (move_ijs) {
+            move_ijs[4 * moves] = bi;
+            move_ijs[4 * moves + 1] = bj;
+            move_ijs[4 * moves + 2] = bip;
+            move_ijs[4 * moves + 3] = bjp;
+        }
         Z[bi * M + bjp] = 1;
         Z[bip * M + bj] = 1;
         Z[bip * M + bjp] = 0;
@@ -229,6 +285,13 @@ static int round_block(const float* S, const float* A, int N, int M, int L,
             }
         if (!found) return OR_ERR_INVARIANT; /* cannot happen while I holds */
         if (move_scores) move_scores[info[1] + info[2]] = best;
+        if (move_ijs) {
+            const int k = info[1] + info[2];
+            move_ijs[4 * k] = i;
+            move_ijs[4 * k + 1] = j;
+            move_ijs[4 * k + 2] = bip;
+            move_ijs[4 * k + 3] = bjp;
+        }
         Z[i * M + bjp] = 1;
         Z[bip * M + j] = 1;
         Z[bip * M + bjp] = 0;
@@ -319,7 +382,7 @@ static int block_feasible(const uint8_t* Z, int N, int M) {
 static int round_block_ex(const float* S, const float* A, int N, int M, int L, int K,
                           const uint8_t* prev, uint8_t* Z, int* order, int* info,
                           float* gains) {
-    int st = round_block(S, A, N, M, L, Z, order, info, NULL, NULL);
+    int st = round_block(S, A, N, M, L, Z, order, info, NULL, NULL, NULL);
     info[3] = info[4] = 0;
     if (st != OR_OK) return st;
     info[3] = polish_block(A, M, K, Z, gains);
@@ -498,12 +561,48 @@ int oracle_dykstra(const float* W, int64_t rows, int64_t cols, int64_t ld, int N
 }
 
 /* One block of rounding on dense M*M arrays (S32 and A row-major); Z gets the
- * 0/1 mask; info as in round_block.                                          */
+ * 0/1 mask; info and the optional move traces (NULL = not wanted) as in
+ * round_block.                                                               */
 int oracle_round_block(const float* S32, const float* A, int N, int M, int ls_steps,
-                       uint8_t* Z, int* info, uint8_t* Zgreedy, float* move_scores) {
+                       uint8_t* Z, int* info, uint8_t* Zgreedy, float* move_scores,
+                       int* move_ijs) {
     if (M < 1 || M > 32 || N < 1 || N > M || ls_steps < 0) return OR_ERR_ARG;
     int order[1024];
-    return round_block(S32, A, N, M, ls_steps, Z, order, info, Zgreedy, move_scores);
+    return round_block(S32, A, N, M, ls_steps, Z, order, info, Zgreedy, move_scores, move_ijs);
+}
+
+/* fp32 mode of the Dykstra steps on the listed blocks (block id as in
+ * oracle_dykstra_blocks); S gets M*M fp32 values per listed block.           */
+int oracle_dykstra_blocks_f32(const float* W, int64_t rows, int64_t cols, int64_t ld,
+                              int N, int M, float tau, int iters,
+                              const int64_t* block_ids, int64_t nblocks, float* S,
+                              int nthreads) {
+    if (check_shape(rows, cols, ld, N, M) || iters < 1 || !(tau >= 0.0f) || !isfinite(tau))
+        return OR_ERR_ARG;
+    const int64_t nbc = cols / M, nb_total = (rows / M) * nbc;
+    for (int64_t b = 0; b < nblocks; ++b)
+        if (block_ids[b] < 0 || block_ids[b] >= nb_total) return OR_ERR_ARG;
+    int status = OR_OK;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+        float A[1024], X[1024], Q[1024];
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t b = 0; b < nblocks; ++b) {
+            int64_t id = block_ids[b];
+            gather_abs(W, ld, id / nbc, id % nbc, M, A);
+            int st = dykstra_block_f32(A, N, M, tau, iters, X, Q);
+            if (st != OR_OK) {
+#pragma omp atomic write
+                status = st;
+                continue;
+            }
+            for (int k = 0; k < M * M; ++k) S[b * M * M + k] = X[k];
+        }
+    }
+    return status;
 }
 
 /* Rounding of every block of a matrix.  S32 [rows x cols] with leading
@@ -533,7 +632,7 @@ int oracle_round(const float* S32, int64_t lds, const float* W, int64_t ld,
             gather_abs(W, ld, bi, bj, M, A);
             for (int i = 0; i < M; ++i)
                 for (int j = 0; j < M; ++j) S[i * M + j] = S32[(bi * M + i) * lds + bj * M + j];
-            int st = round_block(S, A, N, M, ls_steps, Z, order, info, NULL, NULL);
+            int st = round_block(S, A, N, M, ls_steps, Z, order, info, NULL, NULL, NULL);
             if (st != OR_OK) {
 #pragma omp atomic write
                 status = st;

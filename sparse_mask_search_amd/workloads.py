@@ -100,9 +100,19 @@ def _normal_outlier_matrix(rng, rows, cols):
     return W
 
 
-def generate(name: str) -> np.ndarray:
-    """Weights of a named workload: fp32 array, or uint16 bf16 bits."""
+def generate(name: str, rows: int = None) -> np.ndarray:
+    """Weights of a named workload: fp32 array, or uint16 bf16 bits.  With
+    `rows`, only the first rows of the same matrix (the row-chunked bf16
+    workloads stop drawing there; the fp32 ones draw in full and slice)."""
     w = WORKLOADS[name]
+    if rows is not None:
+        if rows <= 0 or rows > w.rows:
+            raise ValueError("rows out of range")
+        if w.M in (16, 32):
+            import dataclasses
+            w = dataclasses.replace(w, rows=rows)
+        else:
+            return np.ascontiguousarray(generate(name)[:rows])
     rng = np.random.default_rng(w.seed)
     if w.M == 4:
         W = rng.standard_normal((w.rows, w.cols))

@@ -53,3 +53,16 @@ def gather_blocks(X, M, ids, cols):
         bi, bj = divmod(int(b), nbc)
         out[n] = X[bi * M:(bi + 1) * M, bj * M:(bj + 1) * M]
     return out
+
+
+S_TOL = 1e-4  # fractional S, max-abs against the fp64 oracle
+
+
+def assert_S_close(S, S64, tol=S_TOL):
+    """GPU S (fp32) within `tol` max-abs of the oracle's fp64 S, shapes equal."""
+    S = np.asarray(S, dtype=np.float64)
+    S64 = np.asarray(S64, dtype=np.float64)
+    assert S.shape == S64.shape, (S.shape, S64.shape)
+    err = float(np.abs(S - S64).max()) if S.size else 0.0
+    assert err < tol, f"max |S - S64| = {err:.3e} >= {tol:g}"
+    return err

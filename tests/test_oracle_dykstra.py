@@ -175,3 +175,56 @@ def test_nonfinite_input_rejected():
     W[1, 1] = np.nan
     with pytest.raises(ValueError):
         oracle.dykstra(W, 2, 4, 20.0, 5)
+
+
+FP32_CONFIGS = [  # workload, first rows drawn, blocks sampled
+    ("2:4-1024x1024-f32", None, 3000),
+    ("4:8-4096x4096-f32", None, 3000),
+    ("8:16-4096x11008-bf16", 512, 1500),
+    ("16:32-8192x28672-bf16", 512, 600),
+    ("16:32-8192x28672-bf16-tau200", 512, 400),
+]
+
+
+def _fp32_gap(W, N, M, tau, T, ids):
+    S64, _ = oracle.dykstra_blocks(W, N, M, tau, T, ids)
+    S32 = oracle.dykstra_blocks_f32(W, N, M, tau, T, ids)
+    return float(np.abs(S64 - S32.astype(np.float64)).max())
+
+
+@pytest.mark.parametrize("name,rows,nblocks", FP32_CONFIGS)
+def test_fp32_mode_within_contract(name, rows, nblocks):
+    """The same Dykstra steps in fp32 (expf/logf) stay within the 1e-4 S bar of
+    the fp64 steps on sampled blocks of each workload (outlier blocks of the
+    4:8 matrix included): the bar sits above the method's own sensitivity to
+    fp32 arithmetic, so it can be met by a correct fp32 implementation.  The
+    measured maximum is printed for the record."""
+    w = wl.WORKLOADS[name]
+    Wb = wl.generate(name, rows=rows)
+    W = wl.bf16_bits_to_f32(Wb) if Wb.dtype == np.uint16 else Wb
+    nb_total = (W.shape[0] // w.M) * (W.shape[1] // w.M)
+    rng = np.random.default_rng(5)
+    ids = np.unique(np.concatenate([rng.choice(nb_total, min(nblocks, nb_total), replace=False),
+                                    [0, nb_total - 1]]))
+    if w.M == 8:  # every block that holds one of the planted outliers
+        big = np.abs(W) >= 0.5
+        bi, bj = np.nonzero(big)
+        ids = np.unique(np.concatenate([ids, (bi // 8) * (W.shape[1] // 8) + bj // 8]))[:6000]
+    gap = _fp32_gap(W, w.N, w.M, w.tau, w.iters, ids)
+    print(f"{name}: max |S64 - S32(fp32 steps)| = {gap:.3e} over {len(ids)} blocks", flush=True)
+    assert gap < 1e-4
+
+
+def test_fp32_mode_7b_projections():
+    """fp32 sensitivity on layer 0 of the 7B-shaped model: an attention
+    projection (8:16) and the MLP down projection (16:32), at tau 30, 150
+    iterations, sampled blocks."""
+    mats = {nm: (N, M, W) for nm, N, M, W in wl.model7b_layer(0, which=("q", "down"))}
+    for nm in ("q", "down"):
+        N, M, Wb = mats[nm]
+        W = wl.bf16_bits_to_f32(Wb[:256])
+        nb_total = (W.shape[0] // M) * (W.shape[1] // M)
+        ids = np.random.default_rng(6).choice(nb_total, 600, replace=False)
+        gap = _fp32_gap(W, N, M, wl.MODEL7B_TAU, wl.MODEL7B_ITERS, ids)
+        print(f"7B layer 0 {nm}: max |S64 - S32(fp32 steps)| = {gap:.3e}", flush=True)
+        assert gap < 1e-4

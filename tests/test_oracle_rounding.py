@@ -6,7 +6,15 @@ budgets remain, then a local search that swaps in (i,j'), (i',j) and removes
 (i',j') when |W_ij'| + |W_i'j| - |W_i'j'| is positive; a feasibility fill
 finishes any block still short of N.  Pins:
 
-* hand-derived 4x4 cases (tests/golden/rounding_cases.json);
+* hand-derived 4x4 cases (tests/golden/rounding_cases.json) and 6x6 cases
+  with a greedy shortfall of 2 (tests/golden/rounding_cases_d2.json: the
+  choice among several deficient pairs, the lexicographic tie order across
+  pairs, the fill's order, the local-search cap and its stop at a
+  non-positive score), checked move by move;
+* on random blocks with small-integer scores (every fp32 score exact), each
+  applied move is the lexicographically smallest maximiser over an
+  exhaustive enumeration of the admissible moves of that step, and the
+  local search stops exactly when the best score is not positive;
 * the tau = 0 closed form: all keys tie, index order gives the block
   diagonal of N x N all-ones tiles;
 * the greedy equals the unique stable b-matching of the key order,
@@ -43,6 +51,84 @@ def test_golden_greedy_and_moves():
         assert np.array_equal(Z, np.array(case["mask"])), case["name"]
         assert list(info) == case["info"], case["name"]
         assert np.array_equal(scores, np.array(case["scores"], np.float32)), case["name"]
+
+
+def test_golden_shortfall_two():
+    with open(os.path.join(GOLDEN, "rounding_cases_d2.json")) as f:
+        g = json.load(f)
+    S = np.array(g["S"], np.float32)
+    for case in g["cases"]:
+        A = np.array(case["A"], np.float32)
+        Z, info, Zg, scores, moves = oracle.round_block(S, A, g["N"], case["L"], trace=True,
+                                                        moves=True)
+        assert np.array_equal(Zg, np.array(g["greedy"])), case["name"]
+        assert list(info) == case["info"], case["name"]
+        assert moves.tolist() == case["moves"], case["name"]
+        assert np.array_equal(scores, np.array(case["scores"], np.float32)), case["name"]
+        assert np.array_equal(Z, np.array(case["mask"])), case["name"]
+
+
+def _admissible(Z, r, c, N, i, j):
+    """(i', j') of every admissible move for the deficient pair (i, j)."""
+    M = Z.shape[0]
+    return [(ip, jp) for ip in range(M) for jp in range(M)
+            if Z[ip, jp] and not Z[i, jp] and not Z[ip, j]]
+
+
+@pytest.mark.parametrize("M,N,L,seed", [(4, 2, 3, 0), (6, 3, 4, 1), (8, 3, 8, 2), (8, 4, 2, 3),
+                                        (8, 5, 8, 4), (16, 6, 6, 5), (16, 8, 16, 6)])
+def test_moves_are_lexicographic_best_bruteforce(M, N, L, seed):
+    """Replays the oracle's moves from its greedy mask.  With integer scores
+    below 2^10 every fp32 sum is exact, so the integer scores here equal the
+    oracle's.  Local search: each move is the lexicographically smallest
+    maximiser of A_ij' + A_i'j - A_i'j' over every deficient row i, deficient
+    column j and admissible (i', j'), its score is positive, and the search
+    ends exactly when the moves reach L, the shortfall reaches 0, or the best
+    score is not positive.  Fill: i and j are the smallest deficient row and
+    column, (i', j') the smallest maximiser."""
+    rng = np.random.default_rng(seed)
+    checked = multi = 0
+    for trial in range(40):
+        A = rng.integers(0, 12, (M, M)).astype(np.float32)
+        S = rng.choice(np.array([0.2, 0.5, 0.7, 1.0], np.float32), (M, M))
+        Z, info, Zg, scores, moves = oracle.round_block(S, A, N, L, trace=True, moves=True)
+        Ai = A.astype(np.int64)
+        Zc = Zg.astype(bool).copy()
+        D, n2, n3 = info
+        assert len(moves) == n2 + n3 == D
+        for k, (i, j, ip, jp) in enumerate(moves):
+            r, c = Zc.sum(1), Zc.sum(0)
+            if k < n2:
+                pairs = [(a, b) for a in range(M) if r[a] < N for b in range(M) if c[b] < N]
+            else:
+                pairs = [(int(np.argmax(r < N)), int(np.argmax(c < N)))]
+            cands = [(Ai[a, q] + Ai[p, b] - Ai[p, q], (a, b, p, q))
+                     for a, b in pairs for p, q in _admissible(Zc, r, c, N, a, b)]
+            best = max(sc for sc, _ in cands)
+            want = min(t for sc, t in cands if sc == best)
+            assert (i, j, ip, jp) == want, (trial, k)
+            assert float(scores[k]) == float(best)
+            if k < n2:
+                assert best > 0
+            Zc[i, jp] = Zc[ip, j] = True
+            Zc[ip, jp] = False
+            checked += 1
+            multi += k < n2 and len(pairs) > 1
+        # the local search stopped for one of its three reasons
+        if n2 < min(L, D):
+            Zs = Zg.astype(bool).copy()
+            for (i, j, ip, jp) in moves[:n2]:
+                Zs[i, jp] = Zs[ip, j] = True
+                Zs[ip, jp] = False
+            r, c = Zs.sum(1), Zs.sum(0)
+            top = max(Ai[a, q] + Ai[p, b] - Ai[p, q]
+                      for a in range(M) if r[a] < N for b in range(M) if c[b] < N
+                      for p, q in _admissible(Zs, r, c, N, a, b))
+            assert top <= 0, trial
+        assert np.array_equal(Zc, Z.astype(bool))
+    assert checked > 0
+    if N >= 4:  # several deficient pairs need N >= 3; random blocks reach them from N = 4
+        assert multi > 0, "no local-search move chose among several deficient pairs"
 
 
 @pytest.mark.parametrize("M,N", [(4, 2), (8, 4), (16, 8), (32, 16), (8, 2)])
