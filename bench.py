@@ -61,30 +61,79 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, W_np, seconds):
-    """The oracle (fp64 Dykstra + rounding, OpenMP over blocks) on the first
-    block-rows of the same matrix, sized to about `seconds` of host time."""
+    """The oracle (fp64 Dykstra + rounding, OpenMP over blocks) on the same
+    matrix: in full when that is expected to take at most about 1.5 x
+    `seconds` of host time, else on its first block-rows sized to `seconds`.
+    Also a single-thread rate on the first block-row."""
     import numpy as np
 
     import oracle
     from sparse_mask_search_amd import workloads as wl
 
-    def run(block_rows):
+    def run(block_rows, nthreads=0):
         rows = block_rows * w.M
         Wf = wl.bf16_bits_to_f32(W_np[:rows]) if W_np.dtype == np.uint16 else W_np[:rows]
         Wf = np.ascontiguousarray(Wf)
         t0 = time.perf_counter()
-        oracle.tsenor(Wf, w.N, w.M, w.tau, w.iters, w.ls_steps)
+        oracle.tsenor(Wf, w.N, w.M, w.tau, w.iters, w.ls_steps, nthreads=nthreads)
         return time.perf_counter() - t0, rows * w.cols
 
     oracle.build(force=False)
-    t1, n1 = run(1)
-    k = int(max(1, min(w.rows // w.M, round(seconds / max(t1, 1e-3)))))
-    t, n = run(k) if k > 1 else (t1, n1)
-    return {"value": n / t / 1e9, "unit": "Gweights/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"first {k} block-row(s): {k * w.M} x {w.cols} = {n} weights, "
-                      f"{k * (w.cols // w.M)} blocks, {t:.1f} s"}
+    cores = oracle.max_threads()
+    nbr = w.rows // w.M
+    t1, n1 = run(1, cores)
+    full = t1 * nbr <= 1.5 * seconds
+    k = nbr if full else int(max(1, min(nbr, round(seconds / max(t1, 1e-3)))))
+    t, n = run(k, cores) if k > 1 else (t1, n1)
+    ts, ns = run(1, nthreads=1)
+    oracle.dykstra(np.zeros((w.M, w.M), np.float32), 1, w.M, 0.0, 1, nthreads=cores)  # restore
+    what = (f"the whole matrix: {w.rows} x {w.cols} = {n} weights, {w.blocks} blocks" if full else
+            f"first {k} of {nbr} block-rows: {k * w.M} x {w.cols} = {n} weights, "
+            f"{k * (w.cols // w.M)} blocks")
+    return {"value": n / t / 1e9, "unit": "Gweights/s", "cores": cores,
+            "kind": "oracle", "sample": f"{what}, {t:.1f} s",
+            "cpu": cpu_model(), "nproc": os.cpu_count(),
+            "single_thread": {"value": ns / ts / 1e9, "unit": "Gweights/s",
+                              "sample": f"first block-row ({w.M} x {w.cols}), {ts:.1f} s"}}
+
+
+def memory_pass(W, M, steps=20):
+    """Rate of the memory side alone (tsenor_bench_memory_pass: W read once
+    by blocks, block max, one bit per weight written) against HBM peak."""
+    import numpy as np
+    import torch
+
+    import sparse_mask_search_amd as sms
+    out = torch.empty((W.shape[0], (W.shape[1] + 31) // 32), dtype=torch.int32, device=W.device)
+    for _ in range(3):
+        sms.memory_pass(W, M, out=out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        sms.memory_pass(W, M, out=out)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    nbytes = W.numel() * W.element_size() + out.numel() * 4
+    gbs = nbytes / (ms / 1e3) / 1e9
+    return {"kernel": "memory_pass_kernel (tsenor_bench_memory_pass)", "kernel_ms": round(ms, 4),
+            "bytes": nbytes, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 MODEL7B = "7b-model-batched"
@@ -114,35 +163,28 @@ def model7b_resident():
     return [m for layer in mats for m in layer]
 
 
-def cpu_baseline_7b(seconds):
-    """The oracle on the first block-rows of every projection of layer 0; the
-    rate is extrapolated to the model's mix of 8:16 and 16:32 weights."""
+def cpu_baseline_7b():
+    """The oracle on every projection of layer 0 in full (202 M weights); the
+    model's time is extrapolated as 32 x layer 0 (the layers differ only in
+    their seeded values)."""
     import numpy as np
 
     import oracle
     from sparse_mask_search_amd import workloads as wl
 
     oracle.build(force=False)
-    mats = list(wl.model7b_layer(0))
-    budget = seconds / len(mats)
-    t_model, n_sample, t_sample = 0.0, 0, 0.0
-    for nm, N, M, W in mats:
-        def run(k):
-            Wf = np.ascontiguousarray(wl.bf16_bits_to_f32(W[:k * M]))
-            t0 = time.perf_counter()
-            oracle.tsenor(Wf, N, M, wl.MODEL7B_TAU, wl.MODEL7B_ITERS, wl.MODEL7B_LS)
-            return time.perf_counter() - t0, Wf.size
-        t1, n1 = run(1)
-        k = int(max(1, min(W.shape[0] // M, round(budget / max(t1, 1e-3)))))
-        t, n = run(k) if k > 1 else (t1, n1)
-        t_model += t / n * W.size * wl.MODEL7B_LAYERS
-        n_sample += n
-        t_sample += t
-    weights = sum(W.size for _, _, _, W in mats) * wl.MODEL7B_LAYERS
-    return {"value": weights / t_model / 1e9, "unit": "Gweights/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"first block-rows of each layer-0 projection: {n_sample} weights in "
-                      f"{t_sample:.1f} s, per-projection rates weighted by the model's weights"}
+    t_layer, n_layer = 0.0, 0
+    for nm, N, M, W in wl.model7b_layer(0):
+        Wf = np.ascontiguousarray(wl.bf16_bits_to_f32(W))
+        t0 = time.perf_counter()
+        oracle.tsenor(Wf, N, M, wl.MODEL7B_TAU, wl.MODEL7B_ITERS, wl.MODEL7B_LS)
+        t_layer += time.perf_counter() - t0
+        n_layer += Wf.size
+    return {"value": n_layer / t_layer / 1e9, "unit": "Gweights/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"layer 0 in full ({n_layer} weights, 7 projections) in {t_layer:.1f} s; "
+                      f"model time extrapolated as 32 x layer 0 = {32 * t_layer:.0f} s",
+            "extrapolated": True, "cpu": cpu_model(), "nproc": os.cpu_count()}
 
 
 def main_7b(args):
@@ -206,8 +248,8 @@ def main_7b(args):
                      "kernel_ms": round(ms, 3), "ops_per_launch": ops},
     }
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-        rec["cpu_baseline"] = cpu_baseline_7b(args.cpu_seconds)
+        log("[bench] cpu baseline (oracle on layer 0 in full)")
+        rec["cpu_baseline"] = cpu_baseline_7b()
     print(json.dumps(rec), flush=True)
 
 
@@ -217,7 +259,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="16:32-8192x28672-bf16")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0,
+                    help="host-time budget of the oracle baseline (the whole matrix when it "
+                         "is expected to take at most 1.5 x this)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--polish-steps", type=int, default=0,
                     help="add the optional 2-opt polish (at most this many swaps per block)")
@@ -304,8 +348,11 @@ def main():
                      "hbm_algorithmic_bytes": hbm_bytes,
                      "hbm_achieved_gbs": round(hbm_bytes / (ms / 1e3) / 1e9, 1)},
     }
+    if w.M in (16, 32):
+        log("[bench] memory side alone")
+        rec["memory_pass"] = memory_pass(W, w.M)
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
+        log(f"[bench] cpu baseline (oracle, budget ~{args.cpu_seconds:.0f} s)")
         rec["cpu_baseline"] = cpu_baseline(w, W_np, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 

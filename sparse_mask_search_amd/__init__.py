@@ -15,7 +15,8 @@ Transposable N:M Sparse Masks" (arXiv 2505.23949), "What carries the argument".
 from __future__ import annotations
 
 from ._lib import (F32, BF16, TsenorError, compress24, exact, lib, library_path, mask,
-                   mask_batched, mask_noalloc, round_mask, spmm24, unpack, version)
+                   mask_batched, mask_noalloc, memory_pass, round_mask, spmm24, unpack, version)
 
 __all__ = ["F32", "BF16", "TsenorError", "compress24", "exact", "lib", "library_path", "mask",
-           "mask_batched", "mask_noalloc", "round_mask", "spmm24", "unpack", "version"]
+           "mask_batched", "mask_noalloc", "memory_pass", "round_mask", "spmm24", "unpack",
+           "version"]

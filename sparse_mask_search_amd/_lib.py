@@ -64,6 +64,8 @@ def lib():
         l.tsenor_mask_batched_ex.argtypes = [ctypes.POINTER(_Matrix), _I, _F, _I, _I, _I,
                                              ctypes.POINTER(_P), _P]
         l.tsenor_mask_batched_ex.restype = _I
+        l.tsenor_bench_memory_pass.argtypes = [_P, _I, _I64, _I64, _I64, _I, _P, _P]
+        l.tsenor_bench_memory_pass.restype = _I
         l.tsenor_status_str.argtypes = [_I]
         l.tsenor_status_str.restype = ctypes.c_char_p
         l.tsenor_last_error.argtypes = []
@@ -312,6 +314,21 @@ def mask_batched(items, tau: float, iters: int, ls_steps: int, return_frac: bool
     if st != 0:
         raise TsenorError(st, where)
     return res
+
+
+def memory_pass(W, M: int, out=None, stream=None):
+    """Measurement only (tsenor_bench_memory_pass): the memory side of the mask
+    search alone -- W read once by M x M blocks, the block max of |W|, and the
+    packed bits (2|W| >= block max) written in the mask layout."""
+    dt = _weights(W)
+    rows, cols = W.shape
+    out = _mask_buffer(W, out)
+    st = lib().tsenor_bench_memory_pass(ctypes.c_void_p(W.data_ptr()), dt, rows, cols,
+                                        W.stride(0), M, ctypes.c_void_p(out.data_ptr()),
+                                        _stream(stream))
+    if st != 0:
+        raise TsenorError(st, "tsenor_bench_memory_pass")
+    return out
 
 
 def unpack(mask_words, cols: int):

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "tsenor.h"
+#include "tsenor_bench.h"
 #include "tsenor_internal.h"
 
 using tsenor::MatJob;
@@ -618,6 +619,21 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
         }
     }
     return record_end(*st, s);
+}
+
+int tsenor_bench_memory_pass(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                             int M, uint32_t* mask_out, void* stream) {
+    if (W == nullptr || mask_out == nullptr) return TSENOR_ERR_NULL;
+    if (dtype != TSENOR_F32 && dtype != TSENOR_BF16) return TSENOR_ERR_DTYPE;
+    if (M != 16 && M != 32) return TSENOR_ERR_NM;
+    const int64_t es = dtype == TSENOR_BF16 ? 2 : 4;
+    if (rows <= 0 || cols <= 0 || rows % M != 0 || cols % M != 0 || ld < cols ||
+        rows > (int64_t(1) << 40) / ld || (reinterpret_cast<uintptr_t>(W) & 15u) != 0 ||
+        (ld * es) % 16 != 0)
+        return TSENOR_ERR_SHAPE;
+    hipError_t e = (hipError_t)tsenor::launch_memory_pass(W, dtype == TSENOR_BF16, rows, cols, ld,
+                                                          M, mask_out, (cols + 31) / 32, stream);
+    return e == hipSuccess ? TSENOR_OK : hip_fail(e, "memory pass kernel launch");
 }
 
 const char* tsenor_status_str(int status) {

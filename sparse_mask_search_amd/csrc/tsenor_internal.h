@@ -64,6 +64,13 @@ int occupancy_exact(int M, int bf16);
 int launch_count_nonfinite(const void* p, int bf16, int64_t rows, int64_t cols, int64_t ld,
                            int* count, int grid, void* stream);
 
+// Measurement only (tsenor_bench.hip): the memory side of the mask search
+// alone -- W read once by M x M blocks (M = 16 or 32; 16-byte aligned rows),
+// block max of |W|, one bit per weight (2|W| >= block max) into `mask`
+// ([rows][wpr] words).
+int launch_memory_pass(const void* W, int bf16, int64_t rows, int64_t cols, int64_t ld, int M,
+                       uint32_t* mask, int64_t wpr, void* stream);
+
 // 2:4 consumer (tsenor_spmm.hip).
 int launch_compress24(const uint16_t* W, int64_t ld, const uint32_t* mask, int64_t wpr,
                       int64_t rows, int64_t k, int trans, uint16_t* vals, uint32_t* meta, int* bad,

@@ -1,13 +1,27 @@
 """Quality and cost of the method against the exact per-block optimum.
 
     python -m sparse_mask_search_amd.eval_quality [--workload NAME] [--polish K ...]
+    python -m sparse_mask_search_amd.eval_quality --sweep [--workload NAME]
+    python -m sparse_mask_search_amd.eval_quality --keep-better [--workload NAME]
 
-For a synthetic workload (see workloads.py) it times the method
+Default mode: for a synthetic workload (see workloads.py) it times the method
 (tsenor_mask_ex with at most K polish swaps per block), then certifies the
 exact optimum of every block with tsenor_exact started from the method's mask,
 and reports the relative gap (optimum - kept |W|) / optimum over all blocks,
 plus the time of the exact solver from the method's mask and from a circulant
-start.  One JSON line per measurement.  Everything runs on the GPU.
+start.
+
+--sweep: the sensitivity of quality and time to the method's three free
+parameters (the TSENOR review's referee report asks for it: tau, the
+iteration count T and the local-search steps L): every (tau, T, L) of the
+grid, gap against the certified optimum of every block and method time.
+
+--keep-better: how often the keep-better safeguard takes the previous mask
+when masks are recomputed on successively perturbed weights W_{k+1} =
+W_k + eps * |W_k| * noise (a stand-in for weights that drift between pruning
+steps), as the fraction of blocks whose result is the previous mask.
+
+One JSON line per measurement.  Everything runs on the GPU.
 """
 import argparse
 import json
@@ -35,9 +49,67 @@ def _timed(torch, fn, reps=1):
     return out, (time.perf_counter() - t0) / reps
 
 
+def _gaps(torch, got, opt):
+    ok = ~torch.isnan(opt)
+    gap = ((opt - got) / torch.where(opt > 0, opt, torch.ones_like(opt)))[ok]
+    return {"gap_mean": float(gap.mean()), "gap_median": float(gap.median()),
+            "gap_p99": float(torch.quantile(gap.float(), 0.99)), "gap_max": float(gap.max()),
+            "blocks_optimal": float((gap <= 1e-12).double().mean()),
+            "uncertified_blocks": int((~ok).sum())}
+
+
+SWEEP_TAU = (20.0, 40.0, 80.0, 200.0)
+SWEEP_T = (50, 100, 200, 300)
+SWEEP_L = (0, 10, 32)
+
+
+def sweep(torch, W, w, args):
+    """Gap and time over the (tau, T, L) grid; the optimum is certified once."""
+    A64 = W.float().abs().double()
+    m0, _ = L.mask(W, w.N, w.M, w.tau, w.iters, w.ls_steps)
+    _, opt = L.exact(W, w.N, w.M, start=m0, max_cancel=args.max_cancel, return_objective=True)
+    torch.cuda.synchronize()
+    for tau in SWEEP_TAU:
+        for T in SWEEP_T:
+            for Ls in SWEEP_L:
+                (m, _), t_m = _timed(torch, lambda: L.mask(W, w.N, w.M, tau, T, Ls), reps=3)
+                got = _block_objective(torch, m, A64, w.rows, w.cols, w.M)
+                rec = {"mode": "sweep", "workload": w.name, "tau": tau, "iters": T,
+                       "ls_steps": Ls, "method_ms": round(t_m * 1e3, 3)}
+                rec.update(_gaps(torch, got, opt))
+                print(json.dumps(rec), flush=True)
+
+
+def keep_better(torch, W, w, args, eps_list=(0.001, 0.01, 0.1), steps=4, seed=0):
+    """Fraction of blocks that keep the previous mask over successive steps."""
+    gen = torch.Generator(device=W.device).manual_seed(seed)
+    nblocks = (w.rows // w.M) * (w.cols // w.M)
+    for eps in eps_list:
+        Wk = W.clone()
+        prev, _ = L.mask(Wk, w.N, w.M, w.tau, w.iters, w.ls_steps)
+        prev = prev.clone()
+        for k in range(1, steps + 1):
+            noise = torch.randn(Wk.shape, device=W.device, generator=gen, dtype=torch.float32)
+            Wk = (Wk.float() + eps * Wk.float().abs() * noise).to(W.dtype)
+            fresh, _ = L.mask(Wk, w.N, w.M, w.tau, w.iters, w.ls_steps)
+            kept, _ = L.mask(Wk, w.N, w.M, w.tau, w.iters, w.ls_steps, prev_mask=prev)
+            torch.cuda.synchronize()
+            # a block keeps the previous mask exactly where the two results differ
+            Zd = L.unpack(fresh ^ kept, w.cols)
+            blk = Zd.reshape(w.rows // w.M, w.M, w.cols // w.M, w.M).any(3).any(1)
+            rec = {"mode": "keep_better", "workload": w.name, "eps": eps, "step": k,
+                   "blocks": nblocks, "kept_previous": int(blk.sum()),
+                   "kept_fraction": float(blk.double().mean())}
+            print(json.dumps(rec), flush=True)
+            prev = kept.clone()
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--workload", default="16:32-8192x28672-bf16", choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--sweep", action="store_true", help="tau x T x L grid")
+    ap.add_argument("--keep-better", action="store_true",
+                    help="keep-better trigger rate on successively perturbed weights")
     ap.add_argument("--polish", type=int, action="append", default=None,
                     help="polish steps to evaluate (repeatable; default 0 and 8)")
     ap.add_argument("--max-cancel", type=int, default=100000)
@@ -52,6 +124,10 @@ def main(argv=None):
         W = torch.from_numpy(Wn.view(np.int16)).cuda().view(torch.bfloat16)
     else:
         W = torch.from_numpy(Wn).cuda()
+    if args.sweep:
+        return sweep(torch, W, w, args)
+    if args.keep_better:
+        return keep_better(torch, W, w, args)
     A64 = W.float().abs().double()
     exact_mask, t_exact = _timed(
         torch, lambda: L.exact(W, w.N, w.M, start=None, max_cancel=args.max_cancel,

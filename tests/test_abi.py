@@ -13,19 +13,21 @@ import sparse_mask_search_amd as sms
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tsenor.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "tsenor_bench.h")
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced on the rejected paths
 
 OK, NULL, SHAPE, NM, PARAM, DTYPE, HIP = range(7)
 
 
 def declared():
-    text = open(HEADER).read()
+    text = open(HEADER).read() + open(BENCH_HEADER).read()
     return sorted(set(re.findall(r"^(?:int|const char\*)\s+(tsenor_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert names == ["tsenor_compress24", "tsenor_exact", "tsenor_last_error", "tsenor_mask",
+    assert names == ["tsenor_bench_memory_pass", "tsenor_compress24", "tsenor_exact",
+                     "tsenor_last_error", "tsenor_mask",
                      "tsenor_mask_batched", "tsenor_mask_batched_ex", "tsenor_mask_ex",
                      "tsenor_mask_noalloc", "tsenor_round", "tsenor_spmm24", "tsenor_status_str",
                      "tsenor_version"]
@@ -157,3 +159,15 @@ def test_binding_requires_device_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(TypeError):
         sms.mask(torch.zeros(8, 8), 2, 4, 20.0, 5, 2)
+
+
+def test_memory_pass_rejects():
+    """The measurement-only memory pass validates on the host before any HIP call."""
+    l = sms.lib()
+    r = lambda W=FAKE, dt=1, rows=64, cols=64, ld=64, M=32, mask=FAKE: l.tsenor_bench_memory_pass(
+        W, dt, rows, cols, ld, M, mask, None)
+    assert r(W=None) == NULL and r(mask=None) == NULL
+    assert r(dt=3) == DTYPE
+    assert r(M=8) == NM and r(M=4) == NM
+    assert r(rows=48) == SHAPE and r(ld=60) == SHAPE and r(ld=68) == SHAPE  # 68*2 % 16 != 0
+    assert r(W=ctypes.c_void_p(0x1002)) == SHAPE  # 16-byte alignment
