@@ -55,7 +55,7 @@ namespace {
 // blocks.  Row sums are completed across the H lanes of a row group by DPP
 // moves, column sums across the G = M/R row groups by a DPP reduce-scatter.
 template <int M> struct Geo;
-template <> struct Geo<4> { static constexpr int R = 4, H = 1; };
+template <> struct Geo<4> { static constexpr int R = 2, H = 1; };
 template <> struct Geo<8> { static constexpr int R = 8, H = 1; };
 template <> struct Geo<16> { static constexpr int R = 4, H = 1; };
 template <> struct Geo<32> { static constexpr int R = 8, H = 2; };
@@ -113,16 +113,33 @@ constexpr float kDeepLog2 = -100.0f;
 // The butterfly tiles broadcast each cycle's new column scales through LDS:
 // one row of M floats per block of the wave.
 template <int M> constexpr int dyk_lds_floats() { return kBfly<M> ? kBPG<M> * M : 0; }
-static_assert(kL<4> == 1 && kL<8> == 1, "blocks of one lane need no column exchange");
+static_assert(kL<8> == 1, "blocks of one lane need no column exchange");
+// M = 4: the rows of a block are spread over G = 4 / R lanes (all four
+// columns each), so a wave holds 64 / G blocks and a 2:4 matrix fills G times
+// the waves of one lane per block.  The column totals meet in log2(G)
+// exchanges (lane ^ 1, lane ^ 2), after which every lane of the block holds
+// the same totals (each level adds a + b in one lane and b + a in its
+// partner) and updates all four column scales itself.
+template <int M> constexpr bool kPairCols = (M == 4);
+static_assert(kH<4> == 1 && kCW<4> == 4 && (kG<4> == 2 || kG<4> == 4), "the layout of M = 4");
+// Totals over the G lanes of an M = 4 block for each column.
+template <int G, bool MAXOP>
+__device__ __forceinline__ void col_pair_allreduce(float (&x)[4]);
 // Rounding staging: block q of a pass at q*kStageBlk, row i at i*(M+4); the
 // block stride is M (mod 32) apart so that column reads of the blocks that
 // share a 32-lane half hit distinct banks.
-template <int M> constexpr int kStageRow = M + 4;
-template <int M> constexpr int kStageBlk = M * (M + 4) + (M < 32 ? M : 0);
+template <int M> constexpr int kStageRow = (M == 4) ? 4 : M + 4;
+template <int M> constexpr int kStageBlk = (M == 4) ? 16 : M * (M + 4) + (M < 32 ? M : 0);
+// Blocks the staging area holds: one rounding pass (64 / M blocks), except
+// for M = 4, where the solve exports the S of its whole group (32 blocks, two
+// passes) straight into LDS instead of the workspace slot: small blocks give
+// a wave too little work to hide the slot's round trip through memory.
+template <int M> constexpr bool kStageInLds = (M == 4);
+template <int M> constexpr int kStaged = kStageInLds<M> ? kBPG<M> : kWave / M;
 // |W| for the local search follows the staging area: block q, row i at
 // (q*M + i)*(M+1); then one word per lane for the rows of the current mask.
 template <int M> constexpr int rnd_lds_floats() {
-    return (kWave / M) * kStageBlk<M> + (kWave / M) * M * (M + 1) + kWave;
+    return kStaged<M> * kStageBlk<M> + (kWave / M) * M * (M + 1) + kWave;
 }
 template <int M> constexpr int lds_floats() {
     return dyk_lds_floats<M>() > rnd_lds_floats<M>() ? dyk_lds_floats<M>() : rnd_lds_floats<M>();
@@ -275,11 +292,12 @@ __device__ __forceinline__ float swz(float x) {
 
 // Butterfly (M = 16 and 32): on return x[0..3] of every lane hold the column
 // totals (max or sum over the 4 row groups) of those register columns; each
-// column is owned by exactly one lane of the block per row half.  The partner
-// values of a level are fetched together (ds_swizzle), then combined: the
-// same operands and order as a DPP add per column, but measured 2-6% faster
-// in the Dykstra cycle, where the DPP form's issue cost sits in the cycle's
-// serial tail.
+// column is owned by exactly one lane of the block per row half.  The eight
+// partner values of the first level are fetched together (ds_swizzle), then
+// combined: the same operands and order as a DPP add per column, but the
+// moves take no VALU issue slot (2-6% faster in the Dykstra cycle, whose
+// serial tail this is).  The second level's four adds are DPP (a further
+// 1-4%: one LDS round trip fewer in the tail).
 template <int M, bool MAXOP>
 __device__ __forceinline__ void col_reduce_scatter(float (&x)[16]) {
     float y[8];
@@ -288,10 +306,27 @@ __device__ __forceinline__ void col_reduce_scatter(float (&x)[16]) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) x[c] = MAXOP ? fmaxf(x[c], y[c]) : x[c] + y[c];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) y[c] = swz<kSwzG0>(x[c + 4]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = MAXOP ? fmaxf(x[c], y[c]) : x[c] + y[c];
+    for (int c = 0; c < 4; ++c) {
+        const float z = dpp_mov<kCtlG0<M>>(x[c + 4]);
+        x[c] = MAXOP ? fmaxf(x[c], z) : x[c] + z;
+    }
 }
+template <int G, bool MAXOP>
+__device__ __forceinline__ void col_pair_allreduce(float (&x)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float y = dpp_mov<0xB1>(x[c]);  // lane ^ 1
+        x[c] = MAXOP ? fmaxf(x[c], y) : x[c] + y;
+    }
+    if constexpr (G == 4) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float y = dpp_mov<0x4E>(x[c]);  // lane ^ 2
+            x[c] = MAXOP ? fmaxf(x[c], y) : x[c] + y;
+        }
+    }
+}
+
 // Inverse: from the owners' x[0..3], every lane gets x[0..15] for its columns.
 template <int M>
 __device__ __forceinline__ void col_all_gather(float (&x)[16]) {
@@ -440,6 +475,10 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             for (int c = 0; c < CW; ++c) cmax[c] = part[c];
             col_reduce_scatter<M, true>(cmax);
             col_all_gather<M>(cmax);
+        } else if constexpr (kPairCols<M>) {
+#pragma unroll
+            for (int c = 0; c < CW; ++c) cmax[c] = part[c];
+            col_pair_allreduce<kG<M>, true>(cmax);
         } else {
 #pragma unroll
             for (int c = 0; c < CW; ++c) cmax[c] = part[c];
@@ -456,6 +495,10 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             for (int c = 0; c < CW; ++c) csum[c] = part[c];
             col_reduce_scatter<M, false>(csum);
             col_all_gather<M>(csum);
+        } else if constexpr (kPairCols<M>) {
+#pragma unroll
+            for (int c = 0; c < CW; ++c) csum[c] = part[c];
+            col_pair_allreduce<kG<M>, false>(csum);
         } else {
 #pragma unroll
             for (int c = 0; c < CW; ++c) csum[c] = part[c];
@@ -566,7 +609,12 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         // [1/M, M], so checking every 4th cycle against 2^+-40 keeps P V U,
         // U and V far inside the fp32 range.
         bool bad = false;
-        if constexpr (L == 1) {
+        if constexpr (L == 1 || kPairCols<M>) {
+            if constexpr (kPairCols<M>) {  // both lanes of the block get the column totals
+                set_prio<kPrioChain>();
+                col_pair_allreduce<kG<M>, false>(cacc);
+                set_prio<0>();
+            }
 #pragma unroll
             for (int c = 0; c < CW; ++c) V[c] = V[c] * rcpf(cacc[c]);
             if ((it & 3) == 0) {
@@ -664,7 +712,9 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         float s[CW];
 #pragma unroll
         for (int c = 0; c < CW; ++c) s[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
-        float* srow = slot + blk * M * M + (g * R + (r ^ rsw)) * M + h * CW;
+        float* srow = kStageInLds<M>
+                          ? lds + blk * kStageBlk<M> + (g * R + (r ^ rsw)) * kStageRow<M> + h * CW
+                          : slot + blk * M * M + (g * R + (r ^ rsw)) * M + h * CW;
 #pragma unroll
         for (int q = 0; q < CW / 4; ++q)
             *reinterpret_cast<float4*>(srow + 4 * (q ^ sw)) =
@@ -895,10 +945,14 @@ __device__ __forceinline__ uint32_t greedy_rows(const uint32_t (&rpb)[M], const 
 
 // Rounding of the 64/M blocks handled by this pass: lane (q, i) = block q,
 // row i (and column i).  Sb points at the lane's block (row stride sld).
-template <int M, bool BF16>
+// STAGED: the pass's S is already in the staging area at `Ss` (M = 4 in the
+// fused kernel) and row i of the lane's |W| is `apre`; otherwise both rows are
+// loaded here (S from Sb, row stride sld).
+template <int M, bool BF16, bool STAGED>
 __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t sld,
-                                           const MatJob& job, int64_t br, int64_t bc, bool valid,
-                                           int ls_steps, float* __restrict__ lds) {
+                                           const float (&apre)[M], const MatJob& job, int64_t br,
+                                           int64_t bc, bool valid, int ls_steps,
+                                           float* __restrict__ Ss, float* __restrict__ lds) {
     constexpr int G = kWave / M;
     constexpr uint32_t FULL = kFull<M>;
     int lane = threadIdx.x;
@@ -912,23 +966,30 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     // Stage the pass's blocks in LDS, then sort row i and column i by key and
     // keep only the bit of each sorted entry.  Row i of |W| is fetched in the
     // same round trip as row i of S: most blocks need it for the local search.
-    float* Ss = lds;                                                     // [G][M][M+4]
-    float* As = lds + G * kStageBlk<M>;                                  // [G][M][M+1]
-    uint32_t* Zs = reinterpret_cast<uint32_t*>(As + G * M * (M + 1));  // [G][M]
+    // Ss [G][M][kStageRow] (S), As [G][M][M+1] (|W|), Zs [G][M] (mask rows)
+    float* As = lds + kStaged<M> * kStageBlk<M>;
+    uint32_t* Zs = reinterpret_cast<uint32_t*>(As + G * M * (M + 1));
     {
-        float v[M], a[M];
-        load_row_f32<M>(Sb + i * sld, (reinterpret_cast<uintptr_t>(Sb) & 15u) == 0 && (sld & 3) == 0, v);
-        if (valid) {
-            load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, a);
+        float a[M];
+        if constexpr (STAGED) {
+#pragma unroll
+            for (int j = 0; j < M; ++j) a[j] = apre[j];
         } else {
+            float v[M];
+            load_row_f32<M>(Sb + i * sld,
+                            (reinterpret_cast<uintptr_t>(Sb) & 15u) == 0 && (sld & 3) == 0, v);
+            if (valid) {
+                load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, a);
+            } else {
 #pragma unroll
-            for (int j = 0; j < M; ++j) { v[j] = 0.f; a[j] = 0.f; }
+                for (int j = 0; j < M; ++j) { v[j] = 0.f; a[j] = 0.f; }
+            }
+            float* dst = Ss + q * kStageBlk<M> + i * kStageRow<M>;
+#pragma unroll
+            for (int k4 = 0; k4 < M / 4; ++k4)
+                *reinterpret_cast<float4*>(dst + 4 * k4) =
+                    make_float4(v[4 * k4], v[4 * k4 + 1], v[4 * k4 + 2], v[4 * k4 + 3]);
         }
-        float* dst = Ss + q * kStageBlk<M> + i * kStageRow<M>;
-#pragma unroll
-        for (int k4 = 0; k4 < M / 4; ++k4)
-            *reinterpret_cast<float4*>(dst + 4 * k4) =
-                make_float4(v[4 * k4], v[4 * k4 + 1], v[4 * k4 + 2], v[4 * k4 + 3]);
         float* Ai = As + (q * M + i) * (M + 1);
 #pragma unroll
         for (int j = 0; j < M; ++j) Ai[j] = a[j];
@@ -1675,15 +1736,48 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
     const int64_t nbc = job.cols / M;
     const int64_t gpr = (nbc + BPG - 1) / BPG;
     const int64_t br = gl / gpr, bc0 = (gl % gpr) * BPG;
+    constexpr int PASSES = BPG / G;
+    // M = 4: the |W| rows the rounding passes use are loaded before the solve
+    // (their latency is then hidden by it), and the solve exports S into the
+    // LDS staging area of both passes.
+    float apre[kStageInLds<M> ? PASSES : 1][M];
+    if constexpr (kStageInLds<M>) {
+        const int q = (int)threadIdx.x / M, i = (int)threadIdx.x % M;
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int64_t bc = bc0 + p * G + q;
+            if (bc < nbc) {
+                load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0,
+                                      apre[p]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < M; ++j) apre[p][j] = 0.f;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < M; ++j) apre[0][j] = 0.f;
+    }
     dykstra_group<M, BF16>(job, prm, br, bc0, slot, lds);
-    __syncthreads();  // slot stores visible to every lane; LDS free for rounding
+    __syncthreads();  // S stores visible to every lane; LDS free for rounding
     set_prio<kPrioRound>();
+    if constexpr (kStageInLds<M>) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int64_t bc = bc0 + p * G + (int)threadIdx.x / M;
+            round_pass<M, BF16, true>(nullptr, 0, apre[p], job, br, bc, bc < nbc, prm.ls_steps,
+                                      lds + p * G * kStageBlk<M>, lds);
+            __syncthreads();
+        }
+    } else {
 #pragma unroll 1
-    for (int p = 0; p < BPG / G; ++p) {
-        const int lb = p * G + (int)threadIdx.x / M;
-        const int64_t bc = bc0 + lb;
-        round_pass<M, BF16>(slot + lb * M * M, M, job, br, bc, bc < nbc, prm.ls_steps, lds);
-        __syncthreads();
+        for (int p = 0; p < PASSES; ++p) {
+            const int lb = p * G + (int)threadIdx.x / M;
+            const int64_t bc = bc0 + lb;
+            round_pass<M, BF16, false>(slot + lb * M * M, M, apre[0], job, br, bc, bc < nbc,
+                                       prm.ls_steps, lds, lds);
+            __syncthreads();
+        }
     }
     set_prio<0>();
 }
@@ -1713,7 +1807,8 @@ __global__ __launch_bounds__(kWave) void round_kernel(MatJob job, const float* _
         const int64_t bc = (g % gpr) * G + threadIdx.x / M;
         const bool valid = bc < nbc;
         const float* Sb = S + br * M * sld + (valid ? bc : 0) * M;
-        round_pass<M, BF16>(Sb, sld, job, br, bc, valid, ls_steps, lds);
+        const float none[M] = {};
+        round_pass<M, BF16, false>(Sb, sld, none, job, br, bc, valid, ls_steps, lds, lds);
         __syncthreads();
     }
 }
