@@ -61,6 +61,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def timed_steps(step, steps):
+    """Run `steps` steps back to back between two HIP events on the launch
+    stream (torch's current stream, the one the library launches on), with a
+    device synchronisation on both sides.  Returns (ms per step by the
+    events -- the launches' average duration including the gaps between
+    them -- and ms per step by the host clock)."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return a.elapsed_time(b) / steps, wall * 1e3 / steps
+
+
 def cpu_model():
     """The host CPU's model name (Linux /proc/cpuinfo), or the platform string."""
     try:
@@ -114,21 +133,13 @@ def cpu_baseline(w, W_np, seconds):
 def memory_pass(W, M, steps=20):
     """Rate of the memory side alone (tsenor_bench_memory_pass: W read once
     by blocks, block max, one bit per weight written) against HBM peak."""
-    import numpy as np
     import torch
 
     import sparse_mask_search_amd as sms
     out = torch.empty((W.shape[0], (W.shape[1] + 31) // 32), dtype=torch.int32, device=W.device)
     for _ in range(3):
         sms.memory_pass(W, M, out=out)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for a, b in ev:
-        a.record()
-        sms.memory_pass(W, M, out=out)
-        b.record()
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    ms, _ = timed_steps(lambda: sms.memory_pass(W, M, out=out), steps)
     nbytes = W.numel() * W.element_size() + out.numel() * 4
     gbs = nbytes / (ms / 1e3) / 1e9
     return {"kernel": "memory_pass_kernel (tsenor_bench_memory_pass)", "kernel_ms": round(ms, 4),
@@ -212,19 +223,8 @@ def main_7b(args):
         step()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record()
-        step()
-        b.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    ms = float(np.mean(kern_ms))
-    ms_wall = wall * 1e3 / args.steps
-    log(f"[bench] ms/step mean {ms:.2f} (min {min(kern_ms):.2f} max {max(kern_ms):.2f}); wall {ms_wall:.2f}")
+    ms, ms_wall = timed_steps(step, args.steps)
+    log(f"[bench] ms/step on the stream {ms:.2f}; wall {ms_wall:.2f}")
     ops = OPS_PER_ELEM_ITER * elem_iters
     achieved = ops / (ms / 1e3) / 1e12
     rec = {
@@ -300,21 +300,8 @@ def main():
         step()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for a, b in ev:
-        a.record()
-        step()
-        b.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    ms = float(np.mean(kern_ms))
-    ms_wall = wall * 1e3 / args.steps
-    log(f"[bench] kernel ms/step mean {ms:.3f} (min {min(kern_ms):.3f} max {max(kern_ms):.3f}); "
-        f"wall {ms_wall:.3f}")
+    ms, ms_wall = timed_steps(step, args.steps)
+    log(f"[bench] ms/step on the stream {ms:.4f}; wall {ms_wall:.4f}")
 
     gw = w.weights / (ms_wall / 1e3) / 1e9
     ops = OPS_PER_ELEM_ITER * w.weights * (w.iters - 1)
