@@ -945,14 +945,48 @@ __device__ __forceinline__ uint32_t greedy_rows(const uint32_t (&rpb)[M], const 
 
 // Rounding of the 64/M blocks handled by this pass: lane (q, i) = block q,
 // row i (and column i).  Sb points at the lane's block (row stride sld).
-// STAGED: the pass's S is already in the staging area at `Ss` (M = 4 in the
-// fused kernel) and row i of the lane's |W| is `apre`; otherwise both rows are
-// loaded here (S from Sb, row stride sld).
-template <int M, bool BF16, bool STAGED>
+// Row i of a rounding pass's block for one lane: S (from Sb, row stride sld;
+// Sb must be a readable address even for a block past the matrix) and |W|
+// (block column bc of block-row br); zeros for a block past the matrix.
+template <int M, bool BF16>
+__device__ __forceinline__ void load_pass_rows(const float* __restrict__ Sb, int64_t sld,
+                                               const MatJob& job, int64_t br, int64_t bc,
+                                               bool valid, int i, float (&v)[M], float (&a)[M]) {
+    load_row_f32<M>(Sb + i * sld, (reinterpret_cast<uintptr_t>(Sb) & 15u) == 0 && (sld & 3) == 0,
+                    v);
+    if (valid) {
+        load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, a);
+    } else {
+#pragma unroll
+        for (int j = 0; j < M; ++j) { v[j] = 0.f; a[j] = 0.f; }
+    }
+}
+
+// The next pass whose rows round_pass loads ahead (after its own rows are
+// staged), so that their memory latency overlaps this pass's sorts and greedy.
+// Used at M = 8 (eight passes per group; 1-3% faster at 4:8 and 8:16 in A/B
+// runs); at M = 32 the 64 registers it holds through the rounding made the
+// 16:32 launch 2% slower, and at M = 16 it measured the same as none.
+template <int M> constexpr bool kPrefetch = (M == 8);
+struct NextPass {
+    const float* Sb;
+    int64_t sld, bc;
+    bool valid, any;
+};
+
+// How a rounding pass gets its rows: loaded here from Sb (row stride sld) and
+// W; given by the caller (v = S, a = |W|), optionally loading the next pass's
+// rows ahead into vn, an; or S already in the LDS staging at Ss and a given.
+enum RowSource { kRowsLoad = 0, kRowsGiven = 1, kRowsStaged = 2 };
+
+// Rounding of the 64/M blocks of one pass; lane (q, i) = block q, row i.
+template <int M, bool BF16, int SRC>
 __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t sld,
-                                           const float (&apre)[M], const MatJob& job, int64_t br,
-                                           int64_t bc, bool valid, int ls_steps,
-                                           float* __restrict__ Ss, float* __restrict__ lds) {
+                                           const float (&v)[M], const float (&a)[M],
+                                           const MatJob& job, int64_t br, int64_t bc, bool valid,
+                                           int ls_steps, float* __restrict__ Ss,
+                                           float* __restrict__ lds, const NextPass& nx,
+                                           float (&vn)[M], float (&an)[M]) {
     constexpr int G = kWave / M;
     constexpr uint32_t FULL = kFull<M>;
     int lane = threadIdx.x;
@@ -969,32 +1003,29 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     // Ss [G][M][kStageRow] (S), As [G][M][M+1] (|W|), Zs [G][M] (mask rows)
     float* As = lds + kStaged<M> * kStageBlk<M>;
     uint32_t* Zs = reinterpret_cast<uint32_t*>(As + G * M * (M + 1));
-    {
-        float a[M];
-        if constexpr (STAGED) {
-#pragma unroll
-            for (int j = 0; j < M; ++j) a[j] = apre[j];
-        } else {
-            float v[M];
-            load_row_f32<M>(Sb + i * sld,
-                            (reinterpret_cast<uintptr_t>(Sb) & 15u) == 0 && (sld & 3) == 0, v);
-            if (valid) {
-                load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, a);
-            } else {
-#pragma unroll
-                for (int j = 0; j < M; ++j) { v[j] = 0.f; a[j] = 0.f; }
-            }
+    auto stage = [&](const float (&vs)[M], const float (&as)[M]) {
+        if constexpr (SRC != kRowsStaged) {
             float* dst = Ss + q * kStageBlk<M> + i * kStageRow<M>;
 #pragma unroll
             for (int k4 = 0; k4 < M / 4; ++k4)
                 *reinterpret_cast<float4*>(dst + 4 * k4) =
-                    make_float4(v[4 * k4], v[4 * k4 + 1], v[4 * k4 + 2], v[4 * k4 + 3]);
+                    make_float4(vs[4 * k4], vs[4 * k4 + 1], vs[4 * k4 + 2], vs[4 * k4 + 3]);
         }
         float* Ai = As + (q * M + i) * (M + 1);
 #pragma unroll
-        for (int j = 0; j < M; ++j) Ai[j] = a[j];
+        for (int j = 0; j < M; ++j) Ai[j] = as[j];
+    };
+    if constexpr (SRC == kRowsLoad) {
+        float vl[M], al[M];
+        load_pass_rows<M, BF16>(Sb, sld, job, br, bc, valid, i, vl, al);
+        stage(vl, al);
+    } else {
+        stage(v, a);
     }
     rnd_sync<M>();
+    if constexpr (SRC == kRowsGiven) {
+        if (nx.any) load_pass_rows<M, BF16>(nx.Sb, nx.sld, job, br, nx.bc, nx.valid, i, vn, an);
+    }
     uint32_t rpb[M], cpb[M];
     // An opaque zero in the keys' low words: with compile-time constants there
     // the scheduler interleaves both sorts and runs out of registers.
@@ -1761,22 +1792,48 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
     dykstra_group<M, BF16>(job, prm, br, bc0, slot, lds);
     __syncthreads();  // S stores visible to every lane; LDS free for rounding
     set_prio<kPrioRound>();
+    const NextPass none{nullptr, 0, 0, false, false};
     if constexpr (kStageInLds<M>) {
+        float unused[M];
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
             const int64_t bc = bc0 + p * G + (int)threadIdx.x / M;
-            round_pass<M, BF16, true>(nullptr, 0, apre[p], job, br, bc, bc < nbc, prm.ls_steps,
-                                      lds + p * G * kStageBlk<M>, lds);
+            round_pass<M, BF16, kRowsStaged>(nullptr, 0, apre[p], apre[p], job, br, bc, bc < nbc,
+                                             prm.ls_steps, lds + p * G * kStageBlk<M>, lds, none,
+                                             unused, unused);
             __syncthreads();
         }
     } else {
+        // kPrefetch: pass p + 1's rows are loaded during pass p (in round_pass,
+        // after staging).  An opaque lane keeps the row addresses from being
+        // hoisted out of the kernel's group loop (and held through the solve).
+        float v[M], a[M], vn[M], an[M];
+        if constexpr (kPrefetch<M>) {
+            int lane = (int)threadIdx.x;
+            asm volatile("" : "+v"(lane));
+            const int q = lane / M, i = lane % M;
+            load_pass_rows<M, BF16>(slot + q * M * M, M, job, br, bc0 + q, bc0 + q < nbc, i, v,
+                                    a);
 #pragma unroll 1
-        for (int p = 0; p < PASSES; ++p) {
-            const int lb = p * G + (int)threadIdx.x / M;
-            const int64_t bc = bc0 + lb;
-            round_pass<M, BF16, false>(slot + lb * M * M, M, apre[0], job, br, bc, bc < nbc,
-                                       prm.ls_steps, lds, lds);
-            __syncthreads();
+            for (int p = 0; p < PASSES; ++p) {
+                const int64_t bc = bc0 + p * G + q, bcn = bc + G;
+                const NextPass nx{slot + ((p + 1) * G + q) * M * M, M, bcn, bcn < nbc,
+                                  p + 1 < PASSES};
+                round_pass<M, BF16, kRowsGiven>(nullptr, 0, v, a, job, br, bc, bc < nbc,
+                                                prm.ls_steps, lds, lds, nx, vn, an);
+                __syncthreads();
+#pragma unroll
+                for (int j = 0; j < M; ++j) { v[j] = vn[j]; a[j] = an[j]; }
+            }
+        } else {
+#pragma unroll 1
+            for (int p = 0; p < PASSES; ++p) {
+                const int lb = p * G + (int)threadIdx.x / M;
+                const int64_t bc = bc0 + lb;
+                round_pass<M, BF16, kRowsLoad>(slot + lb * M * M, M, v, a, job, br, bc, bc < nbc,
+                                               prm.ls_steps, lds, lds, none, vn, an);
+                __syncthreads();
+            }
         }
     }
     set_prio<0>();
@@ -1802,13 +1859,15 @@ __global__ __launch_bounds__(kWave) void round_kernel(MatJob job, const float* _
     const int64_t nbc = job.cols / M;
     const int64_t gpr = (nbc + G - 1) / G;
     const int64_t ngroups = (job.rows / M) * gpr;
+    const NextPass none{nullptr, 0, 0, false, false};
+    float unused[M];
     for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
         const int64_t br = g / gpr;
         const int64_t bc = (g % gpr) * G + threadIdx.x / M;
         const bool valid = bc < nbc;
         const float* Sb = S + br * M * sld + (valid ? bc : 0) * M;
-        const float none[M] = {};
-        round_pass<M, BF16, false>(Sb, sld, none, job, br, bc, valid, ls_steps, lds, lds);
+        round_pass<M, BF16, kRowsLoad>(Sb, sld, unused, unused, job, br, bc, valid, ls_steps, lds,
+                                       lds, none, unused, unused);
         __syncthreads();
     }
 }
