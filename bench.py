@@ -80,6 +80,26 @@ def timed_steps(step, steps):
     return a.elapsed_time(b) / steps, wall * 1e3 / steps
 
 
+def warm_up(step, count, min_seconds=1.0, cap=5000):
+    """Untimed warmup: `count` steps, or with count None as many steps as fill
+    at least `min_seconds` of wall time (at least 3), so that the GPU clocks
+    have settled before the timed region -- short launches run ~15% slower
+    for the first few tens of milliseconds of a busy GPU.  Returns the number
+    of steps run."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (n < count) if count is not None else (
+            n < 3 or (time.perf_counter() - t0 < min_seconds and n < cap)):
+        step()
+        n += 1
+        if count is None and n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
 def cpu_model():
     """The host CPU's model name (Linux /proc/cpuinfo), or the platform string."""
     try:
@@ -137,8 +157,7 @@ def memory_pass(W, M, steps=20):
 
     import sparse_mask_search_amd as sms
     out = torch.empty((W.shape[0], (W.shape[1] + 31) // 32), dtype=torch.int32, device=W.device)
-    for _ in range(3):
-        sms.memory_pass(W, M, out=out)
+    warm_up(lambda: sms.memory_pass(W, M, out=out), None, min_seconds=0.5)
     ms, _ = timed_steps(lambda: sms.memory_pass(W, M, out=out), steps)
     nbytes = W.numel() * W.element_size() + out.numel() * 4
     gbs = nbytes / (ms / 1e3) / 1e9
@@ -219,10 +238,8 @@ def main_7b(args):
         sms.mask_batched([(W, N, M) for W, N, M, _ in items], wl.MODEL7B_TAU, wl.MODEL7B_ITERS,
                          wl.MODEL7B_LS, outs=[o for _, _, _, o in items])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
+    args.warmup = warm_up(step, args.warmup)
+    log(f"[bench] warmed up with {args.warmup} steps; timing {args.steps} steps")
     ms, ms_wall = timed_steps(step, args.steps)
     log(f"[bench] ms/step on the stream {ms:.2f}; wall {ms_wall:.2f}")
     ops = OPS_PER_ELEM_ITER * elem_iters
@@ -257,7 +274,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: as many as fill 1 s)")
     ap.add_argument("--workload", default="16:32-8192x28672-bf16")
     ap.add_argument("--cpu-seconds", type=float, default=30.0,
                     help="host-time budget of the oracle baseline (the whole matrix when it "
@@ -295,11 +313,8 @@ def main():
     def step():
         sms.mask(W, w.N, w.M, w.tau, w.iters, w.ls_steps, out=out, polish_steps=args.polish_steps)
 
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
+    args.warmup = warm_up(step, args.warmup)
+    log(f"[bench] warmed up with {args.warmup} steps; timing {args.steps} steps")
     ms, ms_wall = timed_steps(step, args.steps)
     log(f"[bench] ms/step on the stream {ms:.4f}; wall {ms_wall:.4f}")
 
