@@ -36,25 +36,32 @@ PEAK_VALU_TOPS = 256 * 128 * 2.4e9 / 1e12
 OPS_PER_ELEM_ITER = 4
 KERNEL_SOURCE = os.path.join(ROOT, "sparse_mask_search_amd", "csrc", "tsenor_kernels.hip")
 # HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this benchmark
-# (profiles/mask_kernel_16x32_8192x28672_bf16.md), valid only for the kernel source
-# they were taken on.
-TRAFFIC = {
-    "16:32-8192x28672-bf16": {
-        "kernel_sha256": "44d5bcbae597b5fd18928972487b9c9fe71f544ac279254fc9a478d48fdf9ef1",
-        "read_bytes": 907017.4375 * 1024 * 2.0, "write_bytes": 968147.953125 * 1024 * 1.0},
+# (profiles/mask_kernel_*.md, profiles/batched_kernel_7b_model_bf16.md): KiB per
+# dispatch scaled by what the same counters read for a 1 GiB device copy (x 2.0
+# read, x 1.0 written), valid only for the kernel source they were taken on.  The
+# 7B-shaped model's entry sums its two launches.
+TRAFFIC_SHA = "09685e1206e42bc70c5828a45167148e6f269b99b927d1946f580118919cba28"
+TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) in KiB per launch
+    "16:32-8192x28672-bf16": (1013289.9375, 1046709.09375),
+    "16:32-8192x28672-bf16-tau200": (2723855.3125, 6737454.59375),
+    "8:16-4096x11008-bf16": (88439.0625, 50912.984375),
+    "4:8-4096x4096-f32": (97124.0, 67892.421875),
+    "2:4-1024x1024-f32": (2138.5, 256.0),
+    "7b-model-batched": (8705383.0625 + 4200156.8125, 2035577.375 + 1783653.921875),
 }
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
 def measured_traffic(workload):
     """Counter-based HBM bytes per launch, or None once the kernel has changed."""
     import hashlib
-    t = TRAFFIC.get(workload)
+    t = TRAFFIC_KIB.get(workload)
     if t is None:
         return None
     with open(KERNEL_SOURCE, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != t["kernel_sha256"]:
+        if hashlib.sha256(f.read()).hexdigest() != TRAFFIC_SHA:
             return None
-    return int(t["read_bytes"] + t["write_bytes"])
+    return int(t[0] * 1024 * FETCH_SCALE + t[1] * 1024 * WRITE_SCALE)
 
 
 def log(*a):
@@ -116,8 +123,9 @@ def cpu_model():
 def cpu_baseline(w, W_np, seconds):
     """The oracle (fp64 Dykstra + rounding, OpenMP over blocks) on the same
     matrix: in full when that is expected to take at most about 1.5 x
-    `seconds` of host time, else on its first block-rows sized to `seconds`.
-    Also a single-thread rate on the first block-row."""
+    `seconds` of host time, else on its first block-rows sized to `seconds`;
+    a sample that runs in less than min(10 s, `seconds`) is repeated until it
+    has.  Also a single-thread rate on the first block-row (repeated to 1 s)."""
     import numpy as np
 
     import oracle
@@ -131,23 +139,35 @@ def cpu_baseline(w, W_np, seconds):
         oracle.tsenor(Wf, w.N, w.M, w.tau, w.iters, w.ls_steps, nthreads=nthreads)
         return time.perf_counter() - t0, rows * w.cols
 
+    def repeated(block_rows, nthreads, min_seconds, first=None):
+        t, n, reps = (first[0], first[1], 1) if first else (0.0, 0, 0)
+        while reps == 0 or t < min_seconds:
+            dt, dn = run(block_rows, nthreads)
+            t, n, reps = t + dt, n + dn, reps + 1
+        return t, n, reps
+
     oracle.build(force=False)
     cores = oracle.max_threads()
     nbr = w.rows // w.M
     t1, n1 = run(1, cores)
     full = t1 * nbr <= 1.5 * seconds
     k = nbr if full else int(max(1, min(nbr, round(seconds / max(t1, 1e-3)))))
-    t, n = run(k, cores) if k > 1 else (t1, n1)
-    ts, ns = run(1, nthreads=1)
+    t, n, reps = repeated(k, cores, min(10.0, seconds), first=(t1, n1) if k == 1 else None)
+    ts, ns, reps1 = repeated(1, 1, 1.0)
     oracle.dykstra(np.zeros((w.M, w.M), np.float32), 1, w.M, 0.0, 1, nthreads=cores)  # restore
-    what = (f"the whole matrix: {w.rows} x {w.cols} = {n} weights, {w.blocks} blocks" if full else
-            f"first {k} of {nbr} block-rows: {k * w.M} x {w.cols} = {n} weights, "
+    what = (f"the whole matrix: {w.rows} x {w.cols} = {n // reps} weights, {w.blocks} blocks"
+            if full else
+            f"first {k} of {nbr} block-rows: {k * w.M} x {w.cols} = {n // reps} weights, "
             f"{k * (w.cols // w.M)} blocks")
+    if reps > 1:
+        what += f", run {reps} times"
     return {"value": n / t / 1e9, "unit": "Gweights/s", "cores": cores,
             "kind": "oracle", "sample": f"{what}, {t:.1f} s",
             "cpu": cpu_model(), "nproc": os.cpu_count(),
             "single_thread": {"value": ns / ts / 1e9, "unit": "Gweights/s",
-                              "sample": f"first block-row ({w.M} x {w.cols}), {ts:.1f} s"}}
+                              "sample": f"first block-row ({w.M} x {w.cols})"
+                                        + (f" run {reps1} times" if reps1 > 1 else "")
+                                        + f", {ts:.1f} s"}}
 
 
 def memory_pass(W, M, steps=20):
@@ -260,7 +280,7 @@ def main_7b(args):
         "blocks_per_s": round(blocks / (ms_wall / 1e3), 1),
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_VALU_TOPS,
                      "unit": "Tops/s", "frac": round(achieved / PEAK_VALU_TOPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(MODEL7B),
                      "kernel": "batched_kernel (one launch per N:M class)",
                      "kernel_ms": round(ms, 3), "ops_per_launch": ops},
     }
