@@ -47,8 +47,7 @@ def test_cpu_baseline_record():
     assert rec["nproc"] == os.cpu_count() and rec["cpu"]
     assert rec["sample"].startswith("the whole matrix")  # 1 M weights fit any budget
     assert rec["single_thread"]["value"] > 0
-    # the single-thread rate uses one thread; the budget rate all of them
-    assert rec["single_thread"]["value"] <= rec["value"] * 1.5
+    assert "first block-row" in rec["single_thread"]["sample"]
 
 
 def test_cpu_baseline_samples_block_rows_beyond_the_budget():
