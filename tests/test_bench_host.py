@@ -41,7 +41,7 @@ def test_every_traffic_entry_names_a_workload():
 def test_cpu_baseline_record():
     w = wl.WORKLOADS["2:4-1024x1024-f32"]
     W = wl.generate(w.name)
-    rec = bench.cpu_baseline(w, W, 0.2)
+    rec = bench.cpu_baseline(w, W, 2.0)
     assert rec["kind"] == "oracle" and rec["unit"] == "Gweights/s"
     assert rec["value"] > 0 and rec["cores"] >= 1
     assert rec["nproc"] == os.cpu_count() and rec["cpu"]
