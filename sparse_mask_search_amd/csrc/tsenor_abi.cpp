@@ -57,10 +57,11 @@ struct DeviceState {
     hipEvent_t jobs_up[kStageRing] = {};  // completion of the upload from each
     int jobs_next = 0;
     size_t jobs_cap = 0;
-    int occ_mask[2][33] = {};
+    int occ_mask[2][33] = {};      // the fused kernel without / with the optional stages
+    int occ_mask_opt[2][33] = {};
     int occ_round[2][33] = {};
     int occ_batched[2][33] = {};
-    int occ_refine[2][33] = {};
+    int occ_batched_opt[2][33] = {};
     int occ_exact[2][33] = {};
     uint32_t* prev_copy = nullptr;  // copy of a previous mask that aliases the output
     size_t prev_cap = 0;            // words
@@ -129,10 +130,11 @@ int acquire_geometry(DeviceState** out, std::unique_lock<std::mutex>* lk) {
         if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
         for (int b = 0; b < 2; ++b)
             for (int M : {4, 8, 16, 32}) {
-                st.occ_mask[b][M] = tsenor::occupancy_mask(M, b);
+                st.occ_mask[b][M] = tsenor::occupancy_mask(M, b, false);
+                st.occ_mask_opt[b][M] = tsenor::occupancy_mask(M, b, true);
                 st.occ_round[b][M] = tsenor::occupancy_round(M, b);
-                st.occ_batched[b][M] = tsenor::occupancy_batched(M, b);
-                st.occ_refine[b][M] = tsenor::occupancy_refine(M, b);
+                st.occ_batched[b][M] = tsenor::occupancy_batched(M, b, false);
+                st.occ_batched_opt[b][M] = tsenor::occupancy_batched(M, b, true);
                 st.occ_exact[b][M] = tsenor::occupancy_exact(M, b);
             }
         st.init = true;
@@ -297,15 +299,19 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
         return st_code;
     MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, frac_out);
     job.prev = prev_mask;
-    const int64_t grid = clamp_grid(groups_of(job), st->num_cu, st->occ_mask[job.bf16][M]);
+    // the optional stages run inside the fused kernel, in its second instance
+    const bool optional = polish_steps > 0 || prev_mask != nullptr;
+    const int64_t grid = clamp_grid(
+        groups_of(job), st->num_cu,
+        optional ? st->occ_mask_opt[job.bf16][M] : st->occ_mask[job.bf16][M]);
     if ((st_code = ensure_scratch(*st, (size_t)grid * (size_t)tsenor::slot_floats(M))) != TSENOR_OK)
         return st_code;
     Params prm;
     prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
     prm.iters = iters;
     prm.ls_steps = ls_steps;
+    prm.polish_steps = polish_steps;
     prm.scratch = st->scratch;
-    const bool refine = polish_steps > 0 || prev_mask != nullptr;
     const size_t words = (size_t)rows * (size_t)job.wpr;
     // a previous mask that the solve overwrites (any overlap with the output)
     // is copied first
@@ -324,16 +330,6 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
     if (e != hipSuccess) {
         (void)record_end(*st, s);
         return hip_fail(e, "mask kernel launch");
-    }
-    if (refine) {
-        const int64_t per_pass = tsenor::kWave / M;
-        const int64_t groups = (rows / M) * ((cols / M + per_pass - 1) / per_pass);
-        const int64_t rgrid = clamp_grid(groups, st->num_cu, st->occ_refine[job.bf16][M]);
-        e = (hipError_t)tsenor::launch_refine(job, polish_steps, (int)rgrid, stream);
-        if (e != hipSuccess) {
-            (void)record_end(*st, s);
-            return hip_fail(e, "refine kernel launch");
-        }
     }
     return record_end(*st, s);
 }
@@ -370,6 +366,7 @@ int tsenor_mask_noalloc(const void* W, int dtype, int64_t rows, int64_t cols, in
     prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
     prm.iters = iters;
     prm.ls_steps = ls_steps;
+    prm.polish_steps = 0;
     prm.scratch = st->fixed_scratch;
     hipError_t e = (hipError_t)tsenor::launch_mask(job, prm, (int)grid, stream);
     return e == hipSuccess ? TSENOR_OK : hip_fail(e, "mask kernel launch");
@@ -531,6 +528,34 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
     e = hipEventSynchronize(st->jobs_up[ring]);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
     MatJob* const table = st->jobs_host[ring];
+    // Previous masks that any of the call's outputs overlaps are copied first,
+    // back to back (the solve of one matrix may overwrite another's previous
+    // mask before its optional stages read it); prev_eff[i] is what matrix i's
+    // descriptor reads.
+    const bool optional = polish_steps > 0 || prev_masks != nullptr;
+    size_t alias_words = 0;
+    std::vector<char> alias(count, 0);
+    if (prev_masks != nullptr)
+        for (int i = 0; i < count; ++i) {
+            if (prev_masks[i] == nullptr) continue;
+            const size_t words = mask_words(mats[i].rows, mats[i].cols);
+            for (int j = 0; j < count && !alias[i]; ++j)
+                alias[i] = overlaps(prev_masks[i], words * 4, mats[j].mask_out,
+                                    mask_words(mats[j].rows, mats[j].cols) * 4);
+            if (alias[i]) alias_words += words;
+        }
+    if (alias_words > 0 && (st_code = ensure_prev_copy(*st, alias_words)) != TSENOR_OK)
+        return st_code;
+    std::vector<const uint32_t*> prev_eff(count, nullptr);
+    if (prev_masks != nullptr) {
+        size_t off = 0;
+        for (int i = 0; i < count; ++i) {
+            prev_eff[i] = prev_masks[i];
+            if (!alias[i]) continue;
+            prev_eff[i] = st->prev_copy + off;
+            off += mask_words(mats[i].rows, mats[i].cols);
+        }
+    }
     // One launch per (M, dtype) class present; the class's descriptors are
     // contiguous in the table, in call order, with group ids counted from 0.
     struct Class { int M, bf16, first, n; int64_t groups, grid; };
@@ -545,38 +570,25 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
                 if (m.M != M || (m.dtype == TSENOR_BF16 ? 1 : 0) != b) continue;
                 MatJob j = make_job(m.W, m.dtype, m.rows, m.cols, m.ld, m.N, m.M, m.mask_out,
                                     m.frac_out);
+                j.prev = prev_eff[i];
                 j.group_begin = c.groups;
                 c.groups += groups_of(j);
                 table[filled++] = j;
                 ++c.n;
             }
             if (c.n == 0) continue;
-            c.grid = clamp_grid(c.groups, st->num_cu, st->occ_batched[b][M]);
+            c.grid = clamp_grid(c.groups, st->num_cu,
+                                optional ? st->occ_batched_opt[b][M] : st->occ_batched[b][M]);
             const int64_t need = c.grid * tsenor::slot_floats(M);
             max_floats = need > max_floats ? need : max_floats;
             cls[ncls++] = c;
         }
     if ((st_code = ensure_scratch(*st, (size_t)max_floats)) != TSENOR_OK) return st_code;
-    // previous masks that any of the call's outputs overlaps are copied first,
-    // back to back (the solve of one matrix may overwrite another's previous
-    // mask before the refine stage reads it)
-    size_t alias_words = 0;
-    std::vector<char> alias(count, 0);
-    if (prev_masks != nullptr)
-        for (int i = 0; i < count; ++i) {
-            if (prev_masks[i] == nullptr) continue;
-            const size_t words = mask_words(mats[i].rows, mats[i].cols);
-            for (int j = 0; j < count && !alias[i]; ++j)
-                alias[i] = overlaps(prev_masks[i], words * 4, mats[j].mask_out,
-                                    mask_words(mats[j].rows, mats[j].cols) * 4);
-            if (alias[i]) alias_words += words;
-        }
-    if (alias_words > 0 && (st_code = ensure_prev_copy(*st, alias_words)) != TSENOR_OK)
-        return st_code;
     Params prm;
     prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
     prm.iters = iters;
     prm.ls_steps = ls_steps;
+    prm.polish_steps = polish_steps;
     prm.scratch = st->scratch;
     if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
     e = hipMemcpyAsync(st->jobs_dev, table, sizeof(MatJob) * (size_t)count,
@@ -584,47 +596,25 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
     if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
     e = hipEventRecord(st->jobs_up[ring], s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
-    std::vector<const uint32_t*> prev_eff(count, nullptr);
-    if (prev_masks != nullptr) {
-        size_t off = 0;
-        for (int i = 0; i < count; ++i) {
-            prev_eff[i] = prev_masks[i];
-            if (!alias[i]) continue;
-            const size_t words = mask_words(mats[i].rows, mats[i].cols);
-            e = hipMemcpyAsync(st->prev_copy + off, prev_masks[i], words * sizeof(uint32_t),
-                               hipMemcpyDeviceToDevice, s);
-            if (e != hipSuccess) {
-                (void)record_end(*st, s);
-                return hip_fail(e, "hipMemcpyAsync(previous mask)");
-            }
-            prev_eff[i] = st->prev_copy + off;
-            off += words;
+    for (int i = 0; i < count; ++i) {
+        if (!alias[i]) continue;
+        e = hipMemcpyAsync(const_cast<uint32_t*>(prev_eff[i]), prev_masks[i],
+                           mask_words(mats[i].rows, mats[i].cols) * sizeof(uint32_t),
+                           hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) {
+            (void)record_end(*st, s);
+            return hip_fail(e, "hipMemcpyAsync(previous mask)");
         }
     }
     // The launches run in stream order, so they share the workspace.
     for (int k = 0; k < ncls; ++k) {
         const Class& c = cls[k];
         e = (hipError_t)tsenor::launch_batched(st->jobs_dev + c.first, c.n, c.groups, c.M, c.bf16,
-                                               prm, (int)c.grid, stream);
+                                               prm, optional, (int)c.grid, stream);
         if (e != hipSuccess) {
             // earlier classes may be in flight: keep the workspace ordering
             (void)record_end(*st, s);
             return hip_fail(e, "batched kernel launch");
-        }
-    }
-    // optional stages, one refine launch per matrix that has any
-    for (int i = 0; i < count && (polish_steps > 0 || prev_masks != nullptr); ++i) {
-        if (polish_steps == 0 && prev_eff[i] == nullptr) continue;
-        const tsenor_matrix& m = mats[i];
-        MatJob job = make_job(m.W, m.dtype, m.rows, m.cols, m.ld, m.N, m.M, m.mask_out, nullptr);
-        job.prev = prev_eff[i];
-        const int64_t per_pass = tsenor::kWave / m.M;
-        const int64_t groups = (m.rows / m.M) * ((m.cols / m.M + per_pass - 1) / per_pass);
-        const int64_t rgrid = clamp_grid(groups, st->num_cu, st->occ_refine[job.bf16][m.M]);
-        e = (hipError_t)tsenor::launch_refine(job, polish_steps, (int)rgrid, stream);
-        if (e != hipSuccess) {
-            (void)record_end(*st, s);
-            return hip_fail(e, "refine kernel launch");
         }
     }
     return record_end(*st, s);

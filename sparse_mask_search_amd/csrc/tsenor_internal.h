@@ -23,6 +23,7 @@ struct Params {
     float tau_log2e;    // tau * log2(e): the Gibbs exponent in base 2
     int32_t iters;
     int32_t ls_steps;
+    int32_t polish_steps;  // optional 2-opt swaps per block (0: none)
     float* scratch;     // one slot of slot_floats(M) floats per workgroup
 };
 
@@ -39,12 +40,12 @@ int blocks_per_group(int M);
 int64_t slot_floats(int M);
 
 // Host-side launchers (tsenor_kernels.hip).  They return a hipError_t value.
+// The fused kernel runs the optional stages -- at most prm.polish_steps 2-opt
+// swaps per block, then keeping job.prev where it is feasible and better (if
+// non-null) -- in a separate instance, chosen when either is asked for.
 int launch_mask(const MatJob& job, const Params& prm, int grid, void* stream);
 int launch_round(const MatJob& job, const float* S, int64_t lds, int ls_steps, int grid,
                  void* stream);
-// Optional stages on job.mask in place: at most polish_steps 2-opt swaps per
-// block, then keep job.prev where it is feasible and better (if non-null).
-int launch_refine(const MatJob& job, int polish_steps, int grid, void* stream);
 // Exact optimum of every block by negative-cycle canceling from `start` (a
 // feasible mask, or nullptr for a circulant start) into job.mask; per-block
 // objectives (fp64, NaN if not proven within max_cancel cancellations) to obj
@@ -52,12 +53,11 @@ int launch_refine(const MatJob& job, int polish_steps, int grid, void* stream);
 int launch_exact(const MatJob& job, const uint32_t* start, double* obj, int max_cancel, int grid,
                  void* stream);
 int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int M, int bf16,
-                   const Params& prm, int grid, void* stream);
+                   const Params& prm, bool optional_stages, int grid, void* stream);
 // Number of 64-lane workgroups of each kernel that fit on one CU at once.
-int occupancy_mask(int M, int bf16);
+int occupancy_mask(int M, int bf16, bool optional_stages);
 int occupancy_round(int M, int bf16);
-int occupancy_batched(int M, int bf16);
-int occupancy_refine(int M, int bf16);
+int occupancy_batched(int M, int bf16, bool optional_stages);
 int occupancy_exact(int M, int bf16);
 // Writes to *count (device) the number of non-finite elements of a row-major
 // fp32 / bf16 matrix; two launches on `stream`.

@@ -943,6 +943,225 @@ __device__ __forceinline__ uint32_t greedy_rows(const uint32_t (&rpb)[M], const 
     return Rmask & Amask;
 }
 
+// ---------------------------------------------------------------- optional stages
+// The 2-opt polish keeps per block a triangular table of the best swap gain
+// of every row pair (4-byte keys); the keep-better sums reuse its area.
+template <int M> constexpr int kPairs = M * (M - 1) / 2;
+template <int M>
+__device__ __forceinline__ int tri(int a, int b) { return a * M - a * (a + 1) / 2 + (b - a - 1); }
+template <int M> constexpr int ref_tab_floats() {
+    constexpr int tabs = (kWave / M) * kPairs<M>, sums = 2 * 2 * kWave;
+    return tabs > sums ? tabs : sums;
+}
+
+// The optional stages R4 (2-opt polish, at most polish_steps swaps) and R5
+// (keep the caller's previous mask where it is feasible and better) on the
+// finished mask row Z of lane (q, i) = block q, row i of a pass of 64/M
+// blocks: |W| rows staged in As ([G][M][M+1]), mask rows in Zs ([G][M]), and
+// tab_area an 8-byte aligned LDS area of ref_tab_floats<M>() floats that
+// nothing else uses meanwhile.  Returns the lane's final mask row.
+template <int M>
+__device__ __forceinline__ uint32_t refine_block(uint32_t Z, const MatJob& job, int64_t br,
+                                                 int64_t bc, bool valid, int polish_steps,
+                                                 const float* __restrict__ As,
+                                                 uint32_t* __restrict__ Zs,
+                                                 uint64_t* __restrict__ tab_area, int lane) {
+    constexpr uint32_t FULL = kFull<M>;
+    const int q = lane / M, i = lane % M;
+    const int N = job.N;
+    // ---- R4: 2-opt polish (optional) ----
+    // A swap takes kept (i, j), (i', j'), i < i', with Z_ij' = Z_i'j = 0, to
+    // (i, j'), (i', j); gain fl(fl(A_ij' - A_i'j') + fl(A_i'j - A_ij)).  Per row
+    // pair the gain is monotone in each rounded difference, so the best gain
+    // is fl(T1 + T2) with T1 = max over j' of the first difference and T2 =
+    // max over j of the second; the smallest j and then j' attaining it give
+    // the lexicographic tie-break.
+    if (polish_steps > 0) {
+        // Gain table: for every row pair {a < b} of the block, the ordered key
+        // of its best swap gain (0 = no improving swap), triangular, pair at
+        // tri<M>(a, b), so row a's pairs are contiguous.  Filled once; after a
+        // swap of rows r1, r2 only the pairs touching r1 or r2 change, and lane
+        // p re-evaluates {p, r1} and {p, r2} -- two pairs per lane per step.
+        // Which (j, j') attains a pair's gain matters only for the pairs tied
+        // at a step's best gain, so it is found then, for those pairs alone.
+        uint32_t* tab = reinterpret_cast<uint32_t*>(tab_area) + q * kPairs<M>;
+        float ai[M];
+        {
+            const float* Ai = As + (q * M + i) * (M + 1);
+#pragma unroll
+            for (int c = 0; c < M; ++c) ai[c] = Ai[c];
+        }
+        Zs[q * M + i] = Z;
+        __syncthreads();
+        // The pair {i, p} (p != i), row p's mask Zp: with a = min(i, p), b =
+        // max(i, p), d_c = fl(A_ac - A_bc) = +-fl(A_ic - A_pc), the second
+        // difference is fl(A_bj - A_aj) = -d_j exactly, so the best gain is
+        // fl(T1 - min over j of d_j), T1 = max over j' of d_j'.
+        auto pair_gain = [&](int p, uint32_t Zp, float& T1) -> float {
+            const bool lo = i < p;
+            const uint32_t Za = lo ? Z : Zp, Zb = lo ? Zp : Z;
+            const uint32_t dj = Za & ~Zb;   // j:  Z_aj = 1, Z_bj = 0
+            const uint32_t dk = Zb & ~Za;   // j': Z_bj' = 1, Z_aj' = 0
+            const float* Ap = As + (q * M + p) * (M + 1);
+            float Dmin = __builtin_inff();
+            T1 = -__builtin_inff();
+#pragma unroll
+            for (int c = 0; c < M; ++c) {
+                const float x = __fsub_rn(ai[c], Ap[c]);
+                const float d = lo ? x : -x;
+                if ((dk >> c) & 1u) T1 = fmaxf(T1, d);
+                if ((dj >> c) & 1u) Dmin = fminf(Dmin, d);
+            }
+            return dj == 0u ? -__builtin_inff() : __fadd_rn(T1, -Dmin);
+        };
+        auto gain_key = [&](int p, uint32_t Zp) -> uint32_t {
+            float T1;
+            const float G = pair_gain(p, Zp, T1);
+            return G > 0.f ? float_to_ord(G) : 0u;
+        };
+        // Fill: lane i takes the partners i+1 .. i+M/2 (mod M), the last one only
+        // for i < M/2 -- every pair exactly once, about M/2 pairs per lane.
+        for (int k = 1; k <= M / 2; ++k) {
+            const int p = (i + k) % M;
+            if (k < M / 2 || i < M / 2) {
+                const int a = i < p ? i : p, b = i < p ? p : i;
+                tab[tri<M>(a, b)] = valid ? gain_key(p, Zs[q * M + p]) : 0u;
+            }
+        }
+        __syncthreads();
+        bool active = valid;
+        for (int step = 0; step < polish_steps && __ballot(active) != 0ull; ++step) {
+            // the best gain of the block: lane i scans the pairs it fills
+            // (the same circulant share, about M/2 independent reads)
+            uint32_t g = 0u;
+#pragma unroll
+            for (int k = 1; k <= M / 2; ++k) {
+                const int p = (i + k) % M;
+                const int a = i < p ? i : p, b = i < p ? p : i;
+                const uint32_t v = (k < M / 2 || i < M / 2) ? tab[tri<M>(a, b)] : 0u;
+                g = v > g ? v : g;
+            }
+            if (!active) g = 0u;
+            const uint32_t gmax = group_max_u32<M>(g);
+            if (active && gmax == 0u) active = false;  // no improving swap left
+            // The lexicographically smallest swap among the pairs at that gain.
+            // lex grows with a first, so only the tied pairs of the smallest a
+            // matter; they are taken one at a time in (a, b) order, each by the
+            // whole block (lane c: column c) -- the same arithmetic as a scan
+            // of the pair's columns, as two group reductions and two ballots.
+            const float G = ord_to_float(gmax);
+            uint32_t tied = 0u;  // bit k - 1: pair k of this lane's share ties
+            if (active) {
+                for (int k = 1; k <= M / 2; ++k) {
+                    const int p = (i + k) % M;
+                    const int a = i < p ? i : p, b = i < p ? p : i;
+                    if ((k < M / 2 || i < M / 2) && tab[tri<M>(a, b)] == gmax) tied |= 1u << (k - 1);
+                }
+            }
+            uint32_t lex = 0xFFFFFFFFu;
+            int amin = M;
+            for (;;) {
+                // smallest remaining tied pair of the block, as a * M + b
+                uint32_t key = 0xFFFFFFFFu;
+                for (uint32_t t = tied; t; t &= t - 1u) {
+                    const int p = (i + __ffs(t)) % M;
+                    const uint32_t ab = i < p ? (uint32_t)(i * M + p) : (uint32_t)(p * M + i);
+                    key = ab < key ? ab : key;
+                }
+                const uint32_t kmin = group_min_u32<M>(key);
+                const bool more = kmin != 0xFFFFFFFFu && (int)(kmin / M) <= amin;
+                if (__ballot(more) == 0ull) break;
+                for (uint32_t t = tied; t; t &= t - 1u) {  // the owner drops it
+                    const int k = __ffs(t), p = (i + k) % M;
+                    const uint32_t ab = i < p ? (uint32_t)(i * M + p) : (uint32_t)(p * M + i);
+                    if (ab == kmin) tied &= ~(1u << (k - 1));
+                }
+                const int a = more ? (int)(kmin / M) : 0, b = more ? (int)(kmin % M) : 1;
+                const float* Aa = As + (q * M + a) * (M + 1);
+                const float* Ab = As + (q * M + b) * (M + 1);
+                const uint32_t Za = Zs[q * M + a], Zb = Zs[q * M + b];
+                const float d = __fsub_rn(Aa[i], Ab[i]);  // d_c = fl(A_ac - A_bc), c = i
+                const bool inJ = ((Za & ~Zb) >> i) & 1u, inK = ((Zb & ~Za) >> i) & 1u;
+                const float T1 = ord_to_float(group_max_u32<M>(inK ? float_to_ord(d) : 0u));
+                const uint32_t hj =
+                    (uint32_t)(__ballot(inJ && __fadd_rn(T1, -d) == G) >> (q * M)) & FULL;
+                const int jb = hj ? __ffs(hj) - 1 : 0;
+                const float t2 = -__fsub_rn(Aa[jb], Ab[jb]);
+                const uint32_t hk =
+                    (uint32_t)(__ballot(inK && __fadd_rn(d, t2) == G) >> (q * M)) & FULL;
+                const int jpb = hk ? __ffs(hk) - 1 : 0;
+                if (more) {
+                    amin = a;
+                    const uint32_t l = (uint32_t)(((a * M + jb) * M + b) * M + jpb);
+                    lex = l < lex ? l : lex;
+                }
+            }
+            __syncthreads();
+            int r1 = -1, r2 = -1;
+            if (active) {
+                const int jp = (int)(lex % M), ip = (int)((lex / M) % M);
+                const int j = (int)((lex / (M * M)) % M), ii = (int)(lex / (M * M * M));
+                if (i == ii) Z = (Z & ~(1u << j)) | (1u << jp);
+                if (i == ip) Z = (Z & ~(1u << jp)) | (1u << j);
+                Zs[q * M + i] = Z;
+                r1 = ii;
+                r2 = ip;
+            }
+            __syncthreads();
+            if (r1 >= 0) {
+                // lane i refreshes {i, r1} and {i, r2}; lane r1 refreshes {r1, r2}
+                const int pa = (i == r1) ? r2 : r1;
+                const int pb = (i == r1 || i == r2) ? -1 : r2;
+                {
+                    const int lo2 = i < pa ? i : pa, hi2 = i < pa ? pa : i;
+                    if (i != r2 || pa != r1) tab[tri<M>(lo2, hi2)] = gain_key(pa, Zs[q * M + pa]);
+                }
+                if (pb >= 0) {
+                    const int lo2 = i < pb ? i : pb, hi2 = i < pb ? pb : i;
+                    tab[tri<M>(lo2, hi2)] = gain_key(pb, Zs[q * M + pb]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- R5: keep the caller's previous mask where it is feasible and better ----
+    // Objective of a block: row sums over j ascending, then over rows i
+    // ascending, both in fp64 (every lane forms the same total from LDS).
+    if (job.prev != nullptr) {
+        const float* Ai = As + (q * M + i) * (M + 1);
+        uint32_t Zp = 0u;
+        if (valid) {
+            const int64_t c0 = bc * M;
+            Zp = (job.prev[(br * M + i) * job.wpr + (c0 >> 5)] >> (int)(c0 & 31)) & FULL;
+        }
+        const bool rows_ok = __popc(Zp) == N;
+        const bool cols_ok = __popc(transpose_bits<M>(Zp, (uint32_t)lane)) == N;
+        const uint64_t okb = __ballot(rows_ok && cols_ok);
+        const bool feasible = ((uint32_t)(okb >> (q * M)) & FULL) == FULL;
+        double rz = 0.0, rp = 0.0;
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+            const double a = (double)Ai[j];
+            if ((Z >> j) & 1u) rz += a;
+            if ((Zp >> j) & 1u) rp += a;
+        }
+        double* sums = reinterpret_cast<double*>(tab_area);  // [G][M][2]; tables are done
+        sums[2 * (q * M + i)] = rz;
+        sums[2 * (q * M + i) + 1] = rp;
+        __syncthreads();
+        double tz = 0.0, tp = 0.0;
+        for (int k = 0; k < M; ++k) {
+            tz += sums[2 * (q * M + k)];
+            tp += sums[2 * (q * M + k) + 1];
+        }
+        __syncthreads();
+        if (valid && feasible && tp > tz) Z = Zp;
+    }
+
+    return Z;
+}
+
 // Rounding of the 64/M blocks handled by this pass: lane (q, i) = block q,
 // row i (and column i).  Sb points at the lane's block (row stride sld).
 // Row i of a rounding pass's block for one lane: S (from Sb, row stride sld;
@@ -980,13 +1199,16 @@ struct NextPass {
 enum RowSource { kRowsLoad = 0, kRowsGiven = 1, kRowsStaged = 2 };
 
 // Rounding of the 64/M blocks of one pass; lane (q, i) = block q, row i.
-template <int M, bool BF16, int SRC>
+// POLISH: the optional stages (refine_block) run on the finished rows before
+// the pack, with the pass's S staging (free by then) as their table area.
+template <int M, bool BF16, int SRC, bool POLISH = false>
 __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t sld,
                                            const float (&v)[M], const float (&a)[M],
                                            const MatJob& job, int64_t br, int64_t bc, bool valid,
                                            int ls_steps, float* __restrict__ Ss,
                                            float* __restrict__ lds, const NextPass& nx,
-                                           float (&vn)[M], float (&an)[M]) {
+                                           float (&vn)[M], float (&an)[M],
+                                           int polish_steps = 0) {
     constexpr int G = kWave / M;
     constexpr uint32_t FULL = kFull<M>;
     int lane = threadIdx.x;
@@ -1286,6 +1508,15 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
         }
     }
 
+    if constexpr (POLISH) {
+        static_assert(kStageInLds<M> ? (kWave / M) * kStageBlk<M> >= ref_tab_floats<M>()
+                                     : kStaged<M> * kStageBlk<M> >= ref_tab_floats<M>(),
+                      "the optional stages' table fits the pass's S staging");
+        rnd_sync<M>();  // every lane is done with the staged S
+        Z = refine_block<M>(Z, job, br, bc, valid, polish_steps, As, Zs,
+                            reinterpret_cast<uint64_t*>(Ss), lane);
+    }
+
     // ---- pack: OR the blocks of one 32-column word together, one store ----
     const int bit0 = (int)((bc * M) & 31);
     uint32_t w = valid ? (Z << bit0) : 0u;
@@ -1293,260 +1524,6 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     if constexpr (M <= 8) w |= xor_lane<8>(w);
     if constexpr (M <= 16) w |= xor_lane<16>(w);
     if (valid && bit0 == 0) job.mask[(br * M + i) * job.wpr + ((bc * M) >> 5)] = w;
-}
-
-// ---------------------------------------------------------------- refine
-// LDS of the refine pass: |W| rows, mask rows, then per block a triangular
-// table of the best swap gain of every row pair (4-byte keys), an area the
-// keep-better sums reuse.
-template <int M> constexpr int kPairs = M * (M - 1) / 2;
-template <int M>
-__device__ __forceinline__ int tri(int a, int b) { return a * M - a * (a + 1) / 2 + (b - a - 1); }
-template <int M> constexpr int ref_tab_offset() {  // in floats, 8-byte aligned
-    return ((kWave / M) * M * (M + 1) + kWave + 1) & ~1;
-}
-template <int M> constexpr int ref_lds_floats() {
-    constexpr int tabs = (kWave / M) * kPairs<M>, sums = 2 * 2 * kWave;
-    return ref_tab_offset<M>() + (tabs > sums ? tabs : sums);
-}
-
-// Optional stages on a finished mask (job.mask), for the 64/M blocks of one
-// pass: lane (q, i) = block q, row i.  |W| rows are staged in LDS like the
-// rounding's; the result is written back to job.mask.
-template <int M, bool BF16>
-__device__ __forceinline__ void refine_pass(const MatJob& job, int64_t br, int64_t bc, bool valid,
-                                            int polish_steps, float* __restrict__ lds) {
-    constexpr int G = kWave / M;
-    constexpr uint32_t FULL = kFull<M>;
-    int lane = threadIdx.x;
-    asm volatile("" : "+v"(lane));
-    const int q = lane / M, i = lane % M;
-    const int N = job.N;
-    // LDS: |W| rows [G][M][M+1], mask rows [G][M], then the polish's pair
-    // tables (the R5 sums reuse that area once the polish is done)
-    float* As = lds;
-    uint32_t* Zs = reinterpret_cast<uint32_t*>(As + G * M * (M + 1));
-    uint64_t* tab_area = reinterpret_cast<uint64_t*>(lds + ref_tab_offset<M>());
-    uint32_t Z = 0u;
-    {
-        float a[M];
-        if (valid) {
-            load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, a);
-            const int64_t c0 = bc * M;
-            Z = (job.mask[(br * M + i) * job.wpr + (c0 >> 5)] >> (int)(c0 & 31)) & FULL;
-        } else {
-#pragma unroll
-            for (int j = 0; j < M; ++j) a[j] = 0.f;
-        }
-        float* Ai = As + (q * M + i) * (M + 1);
-#pragma unroll
-        for (int j = 0; j < M; ++j) Ai[j] = a[j];
-    }
-    __syncthreads();
-
-    // ---- R4: 2-opt polish (optional) ----
-    // A swap takes kept (i, j), (i', j'), i < i', with Z_ij' = Z_i'j = 0, to
-    // (i, j'), (i', j); gain fl(fl(A_ij' - A_i'j') + fl(A_i'j - A_ij)).  Per row
-    // pair the gain is monotone in each rounded difference, so the best gain
-    // is fl(T1 + T2) with T1 = max over j' of the first difference and T2 =
-    // max over j of the second; the smallest j and then j' attaining it give
-    // the lexicographic tie-break.
-    if (polish_steps > 0) {
-        // Gain table: for every row pair {a < b} of the block, the ordered key
-        // of its best swap gain (0 = no improving swap), triangular, pair at
-        // tri<M>(a, b), so row a's pairs are contiguous.  Filled once; after a
-        // swap of rows r1, r2 only the pairs touching r1 or r2 change, and lane
-        // p re-evaluates {p, r1} and {p, r2} -- two pairs per lane per step.
-        // Which (j, j') attains a pair's gain matters only for the pairs tied
-        // at a step's best gain, so it is found then, for those pairs alone.
-        uint32_t* tab = reinterpret_cast<uint32_t*>(tab_area) + q * kPairs<M>;
-        float ai[M];
-        {
-            const float* Ai = As + (q * M + i) * (M + 1);
-#pragma unroll
-            for (int c = 0; c < M; ++c) ai[c] = Ai[c];
-        }
-        Zs[q * M + i] = Z;
-        __syncthreads();
-        // The pair {i, p} (p != i), row p's mask Zp: with a = min(i, p), b =
-        // max(i, p), d_c = fl(A_ac - A_bc) = +-fl(A_ic - A_pc), the second
-        // difference is fl(A_bj - A_aj) = -d_j exactly, so the best gain is
-        // fl(T1 - min over j of d_j), T1 = max over j' of d_j'.
-        auto pair_gain = [&](int p, uint32_t Zp, float& T1) -> float {
-            const bool lo = i < p;
-            const uint32_t Za = lo ? Z : Zp, Zb = lo ? Zp : Z;
-            const uint32_t dj = Za & ~Zb;   // j:  Z_aj = 1, Z_bj = 0
-            const uint32_t dk = Zb & ~Za;   // j': Z_bj' = 1, Z_aj' = 0
-            const float* Ap = As + (q * M + p) * (M + 1);
-            float Dmin = __builtin_inff();
-            T1 = -__builtin_inff();
-#pragma unroll
-            for (int c = 0; c < M; ++c) {
-                const float x = __fsub_rn(ai[c], Ap[c]);
-                const float d = lo ? x : -x;
-                if ((dk >> c) & 1u) T1 = fmaxf(T1, d);
-                if ((dj >> c) & 1u) Dmin = fminf(Dmin, d);
-            }
-            return dj == 0u ? -__builtin_inff() : __fadd_rn(T1, -Dmin);
-        };
-        auto gain_key = [&](int p, uint32_t Zp) -> uint32_t {
-            float T1;
-            const float G = pair_gain(p, Zp, T1);
-            return G > 0.f ? float_to_ord(G) : 0u;
-        };
-        // (a, j, b, j') of the pair {i, p} at gain G: the smallest j attaining
-        // G, then the smallest j' given that j (bit masks of the hits, lowest
-        // bit), as one lexicographic index
-        auto pair_lex = [&](int p, uint32_t Zp, float G) -> uint32_t {
-            const bool lo = i < p;
-            const uint32_t Za = lo ? Z : Zp, Zb = lo ? Zp : Z;
-            const uint32_t dj = Za & ~Zb, dk = Zb & ~Za;
-            const float* Ap = As + (q * M + p) * (M + 1);
-            float T1;
-            (void)pair_gain(p, Zp, T1);
-            uint32_t hj = 0u;
-#pragma unroll
-            for (int c = 0; c < M; ++c) {
-                const float x = __fsub_rn(ai[c], Ap[c]);
-                const float d = lo ? x : -x;
-                hj |= (__fadd_rn(T1, -d) == G) ? (1u << c) : 0u;
-            }
-            const int jb = __ffs(hj & dj) - 1;
-            const float xb = __fsub_rn(As[(q * M + i) * (M + 1) + jb], Ap[jb]);
-            const float t2 = lo ? -xb : xb;  // -d_jb
-            uint32_t hk = 0u;
-#pragma unroll
-            for (int c = 0; c < M; ++c) {
-                const float x = __fsub_rn(ai[c], Ap[c]);
-                const float d = lo ? x : -x;
-                hk |= (__fadd_rn(d, t2) == G) ? (1u << c) : 0u;
-            }
-            const int jpb = __ffs(hk & dk) - 1;
-            const int a = lo ? i : p, b = lo ? p : i;
-            return (uint32_t)(((a * M + jb) * M + b) * M + jpb);
-        };
-        // Fill: lane i takes the partners i+1 .. i+M/2 (mod M), the last one only
-        // for i < M/2 -- every pair exactly once, about M/2 pairs per lane.
-        for (int k = 1; k <= M / 2; ++k) {
-            const int p = (i + k) % M;
-            if (k < M / 2 || i < M / 2) {
-                const int a = i < p ? i : p, b = i < p ? p : i;
-                tab[tri<M>(a, b)] = valid ? gain_key(p, Zs[q * M + p]) : 0u;
-            }
-        }
-        __syncthreads();
-        bool active = valid;
-        for (int step = 0; step < polish_steps && __ballot(active) != 0ull; ++step) {
-            // the best gain of the block: lane i scans the pairs it fills
-            // (the same circulant share, about M/2 independent reads)
-            uint32_t g = 0u;
-#pragma unroll
-            for (int k = 1; k <= M / 2; ++k) {
-                const int p = (i + k) % M;
-                const int a = i < p ? i : p, b = i < p ? p : i;
-                const uint32_t v = (k < M / 2 || i < M / 2) ? tab[tri<M>(a, b)] : 0u;
-                g = v > g ? v : g;
-            }
-            if (!active) g = 0u;
-            const uint32_t gmax = group_max_u32<M>(g);
-            if (active && gmax == 0u) active = false;  // no improving swap left
-            // the lexicographically smallest swap among the pairs at that gain
-            uint32_t lx = 0xFFFFFFFFu;
-            if (active && g == gmax) {
-                const float G = ord_to_float(gmax);
-                for (int k = 1; k <= M / 2; ++k) {
-                    const int p = (i + k) % M;
-                    const int a = i < p ? i : p, b = i < p ? p : i;
-                    if (!(k < M / 2 || i < M / 2) || tab[tri<M>(a, b)] != gmax) continue;
-                    const uint32_t l = pair_lex(p, Zs[q * M + p], G);
-                    lx = l < lx ? l : lx;
-                }
-            }
-            const uint32_t lex = group_min_u32<M>(lx);
-            __syncthreads();
-            int r1 = -1, r2 = -1;
-            if (active) {
-                const int jp = (int)(lex % M), ip = (int)((lex / M) % M);
-                const int j = (int)((lex / (M * M)) % M), ii = (int)(lex / (M * M * M));
-                if (i == ii) Z = (Z & ~(1u << j)) | (1u << jp);
-                if (i == ip) Z = (Z & ~(1u << jp)) | (1u << j);
-                Zs[q * M + i] = Z;
-                r1 = ii;
-                r2 = ip;
-            }
-            __syncthreads();
-            if (r1 >= 0) {
-                // lane i refreshes {i, r1} and {i, r2}; lane r1 refreshes {r1, r2}
-                const int pa = (i == r1) ? r2 : r1;
-                const int pb = (i == r1 || i == r2) ? -1 : r2;
-                {
-                    const int lo2 = i < pa ? i : pa, hi2 = i < pa ? pa : i;
-                    if (i != r2 || pa != r1) tab[tri<M>(lo2, hi2)] = gain_key(pa, Zs[q * M + pa]);
-                }
-                if (pb >= 0) {
-                    const int lo2 = i < pb ? i : pb, hi2 = i < pb ? pb : i;
-                    tab[tri<M>(lo2, hi2)] = gain_key(pb, Zs[q * M + pb]);
-                }
-            }
-            __syncthreads();
-        }
-    }
-
-    // ---- R5: keep the caller's previous mask where it is feasible and better ----
-    // Objective of a block: row sums over j ascending, then over rows i
-    // ascending, both in fp64 (every lane forms the same total from LDS).
-    if (job.prev != nullptr) {
-        const float* Ai = As + (q * M + i) * (M + 1);
-        uint32_t Zp = 0u;
-        if (valid) {
-            const int64_t c0 = bc * M;
-            Zp = (job.prev[(br * M + i) * job.wpr + (c0 >> 5)] >> (int)(c0 & 31)) & FULL;
-        }
-        const bool rows_ok = __popc(Zp) == N;
-        const bool cols_ok = __popc(transpose_bits<M>(Zp, (uint32_t)lane)) == N;
-        const uint64_t okb = __ballot(rows_ok && cols_ok);
-        const bool feasible = ((uint32_t)(okb >> (q * M)) & FULL) == FULL;
-        double rz = 0.0, rp = 0.0;
-#pragma unroll
-        for (int j = 0; j < M; ++j) {
-            const double a = (double)Ai[j];
-            if ((Z >> j) & 1u) rz += a;
-            if ((Zp >> j) & 1u) rp += a;
-        }
-        double* sums = reinterpret_cast<double*>(tab_area);  // [G][M][2]; tables are done
-        sums[2 * (q * M + i)] = rz;
-        sums[2 * (q * M + i) + 1] = rp;
-        __syncthreads();
-        double tz = 0.0, tp = 0.0;
-        for (int k = 0; k < M; ++k) {
-            tz += sums[2 * (q * M + k)];
-            tp += sums[2 * (q * M + k) + 1];
-        }
-        __syncthreads();
-        if (valid && feasible && tp > tz) Z = Zp;
-    }
-
-    // ---- store: OR the blocks of one 32-column word together ----
-    const int bit0 = (int)((bc * M) & 31);
-    uint32_t w = valid ? (Z << bit0) : 0u;
-    if constexpr (M <= 4) w |= xor_lane<4>(w);
-    if constexpr (M <= 8) w |= xor_lane<8>(w);
-    if constexpr (M <= 16) w |= xor_lane<16>(w);
-    if (valid && bit0 == 0) job.mask[(br * M + i) * job.wpr + ((bc * M) >> 5)] = w;
-}
-
-template <int M, bool BF16>
-__global__ __launch_bounds__(kWave) void refine_kernel(MatJob job, int polish_steps) {
-    __shared__ __attribute__((aligned(16))) float lds[ref_lds_floats<M>()];
-    constexpr int G = kWave / M;
-    const int64_t nbc = job.cols / M;
-    const int64_t gpr = (nbc + G - 1) / G;
-    const int64_t groups = (job.rows / M) * gpr;
-    for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
-        const int64_t br = g / gpr, bc = (g % gpr) * G + (int)threadIdx.x / M;
-        refine_pass<M, BF16>(job, br, bc, bc < nbc, polish_steps, lds);
-        __syncthreads();
-    }
 }
 
 // ---------------------------------------------------------------- exact
@@ -1760,7 +1737,7 @@ __global__ __launch_bounds__(kWave) void exact_kernel(MatJob job, const uint32_t
 }
 
 // Whole path for group gl (block-row br, first block column bc0) of one matrix.
-template <int M, bool BF16>
+template <int M, bool BF16, bool POLISH>
 __device__ __forceinline__ void process_group(const MatJob& job, const Params& prm, int64_t gl,
                                               float* slot, float* lds) {
     constexpr int BPG = kBPG<M>, G = kWave / M;
@@ -1798,9 +1775,10 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
             const int64_t bc = bc0 + p * G + (int)threadIdx.x / M;
-            round_pass<M, BF16, kRowsStaged>(nullptr, 0, apre[p], apre[p], job, br, bc, bc < nbc,
-                                             prm.ls_steps, lds + p * G * kStageBlk<M>, lds, none,
-                                             unused, unused);
+            round_pass<M, BF16, kRowsStaged, POLISH>(nullptr, 0, apre[p], apre[p], job, br, bc,
+                                                     bc < nbc, prm.ls_steps,
+                                                     lds + p * G * kStageBlk<M>, lds, none,
+                                                     unused, unused, prm.polish_steps);
             __syncthreads();
         }
     } else {
@@ -1819,8 +1797,9 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
                 const int64_t bc = bc0 + p * G + q, bcn = bc + G;
                 const NextPass nx{slot + ((p + 1) * G + q) * M * M, M, bcn, bcn < nbc,
                                   p + 1 < PASSES};
-                round_pass<M, BF16, kRowsGiven>(nullptr, 0, v, a, job, br, bc, bc < nbc,
-                                                prm.ls_steps, lds, lds, nx, vn, an);
+                round_pass<M, BF16, kRowsGiven, POLISH>(nullptr, 0, v, a, job, br, bc, bc < nbc,
+                                                        prm.ls_steps, lds, lds, nx, vn, an,
+                                                        prm.polish_steps);
                 __syncthreads();
 #pragma unroll
                 for (int j = 0; j < M; ++j) { v[j] = vn[j]; a[j] = an[j]; }
@@ -1830,8 +1809,9 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
             for (int p = 0; p < PASSES; ++p) {
                 const int lb = p * G + (int)threadIdx.x / M;
                 const int64_t bc = bc0 + lb;
-                round_pass<M, BF16, kRowsLoad>(slot + lb * M * M, M, v, a, job, br, bc, bc < nbc,
-                                               prm.ls_steps, lds, lds, none, vn, an);
+                round_pass<M, BF16, kRowsLoad, POLISH>(slot + lb * M * M, M, v, a, job, br, bc,
+                                                       bc < nbc, prm.ls_steps, lds, lds, none,
+                                                       vn, an, prm.polish_steps);
                 __syncthreads();
             }
         }
@@ -1839,7 +1819,7 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
     set_prio<0>();
 }
 
-template <int M, bool BF16>
+template <int M, bool BF16, bool POLISH>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kSolveWaves<M>)))
 void mask_kernel(MatJob job, Params prm) {
     __shared__ __attribute__((aligned(16))) float lds[lds_floats<M>()];
@@ -1848,7 +1828,7 @@ void mask_kernel(MatJob job, Params prm) {
     const int64_t ngroups = (job.rows / M) * ((nbc + BPG - 1) / BPG);
     float* slot = prm.scratch + (int64_t)blockIdx.x * kSlot<M>;
     for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x)
-        process_group<M, BF16>(job, prm, g, slot, lds);
+        process_group<M, BF16, POLISH>(job, prm, g, slot, lds);
 }
 
 template <int M, bool BF16>
@@ -1876,7 +1856,7 @@ __global__ __launch_bounds__(kWave) void round_kernel(MatJob job, const float* _
 // class's matrices with group_begin = prefix sum of their group counts; the
 // grid walks the concatenated group range.  One kernel per class keeps the
 // register allocation of each path as tight as in mask_kernel.
-template <int M, bool BF16>
+template <int M, bool BF16, bool POLISH>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kSolveWaves<M>)))
 void batched_kernel(const MatJob* __restrict__ jobs, int count, int64_t total_groups, Params prm) {
     __shared__ __attribute__((aligned(16))) float lds[lds_floats<M>()];
@@ -1888,7 +1868,7 @@ void batched_kernel(const MatJob* __restrict__ jobs, int count, int64_t total_gr
             if (jobs[mid].group_begin <= g) lo = mid; else hi = mid - 1;
         }
         const MatJob job = jobs[lo];
-        process_group<M, BF16>(job, prm, g - job.group_begin, slot, lds);
+        process_group<M, BF16, POLISH>(job, prm, g - job.group_begin, slot, lds);
     }
 }
 
@@ -1955,9 +1935,15 @@ int blocks_per_group(int M) {
 }
 
 int launch_mask(const MatJob& job, const Params& prm, int grid, void* stream) {
-    TSENOR_DISPATCH(job.M, job.bf16,
-                    hipLaunchKernelGGL((mask_kernel<MM, B>), dim3(grid), dim3(kWave), 0,
-                                       (hipStream_t)stream, job, prm));
+    if (prm.polish_steps > 0 || job.prev != nullptr) {
+        TSENOR_DISPATCH(job.M, job.bf16,
+                        hipLaunchKernelGGL((mask_kernel<MM, B, true>), dim3(grid), dim3(kWave), 0,
+                                           (hipStream_t)stream, job, prm));
+    } else {
+        TSENOR_DISPATCH(job.M, job.bf16,
+                        hipLaunchKernelGGL((mask_kernel<MM, B, false>), dim3(grid), dim3(kWave),
+                                           0, (hipStream_t)stream, job, prm));
+    }
     return (int)hipGetLastError();
 }
 
@@ -1970,18 +1956,32 @@ int launch_round(const MatJob& job, const float* S, int64_t lds, int ls_steps, i
 }
 
 int launch_batched(const MatJob* jobs_dev, int count, int64_t total_groups, int M, int bf16,
-                   const Params& prm, int grid, void* stream) {
-    TSENOR_DISPATCH(M, bf16,
-                    hipLaunchKernelGGL((batched_kernel<MM, B>), dim3(grid), dim3(kWave), 0,
-                                       (hipStream_t)stream, jobs_dev, count, total_groups, prm));
+                   const Params& prm, bool optional_stages, int grid, void* stream) {
+    if (optional_stages) {
+        TSENOR_DISPATCH(M, bf16,
+                        hipLaunchKernelGGL((batched_kernel<MM, B, true>), dim3(grid), dim3(kWave),
+                                           0, (hipStream_t)stream, jobs_dev, count, total_groups,
+                                           prm));
+    } else {
+        TSENOR_DISPATCH(M, bf16,
+                        hipLaunchKernelGGL((batched_kernel<MM, B, false>), dim3(grid),
+                                           dim3(kWave), 0, (hipStream_t)stream, jobs_dev, count,
+                                           total_groups, prm));
+    }
     return (int)hipGetLastError();
 }
 
-int occupancy_mask(int M, int bf16) {
+int occupancy_mask(int M, int bf16, bool optional_stages) {
     int n = 0;
-    TSENOR_DISPATCH(M, bf16,
-                    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mask_kernel<MM, B>,
-                                                                       kWave, 0));
+    if (optional_stages) {
+        TSENOR_DISPATCH(M, bf16,
+                        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &n, mask_kernel<MM, B, true>, kWave, 0));
+    } else {
+        TSENOR_DISPATCH(M, bf16,
+                        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &n, mask_kernel<MM, B, false>, kWave, 0));
+    }
     return n;
 }
 
@@ -1991,13 +1991,6 @@ int occupancy_round(int M, int bf16) {
                     (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, round_kernel<MM, B>,
                                                                        kWave, 0));
     return n;
-}
-
-int launch_refine(const MatJob& job, int polish_steps, int grid, void* stream) {
-    TSENOR_DISPATCH(job.M, job.bf16,
-                    hipLaunchKernelGGL((refine_kernel<MM, B>), dim3(grid), dim3(kWave), 0,
-                                       (hipStream_t)stream, job, polish_steps));
-    return (int)hipGetLastError();
 }
 
 int launch_exact(const MatJob& job, const uint32_t* start, double* obj, int max_cancel, int grid,
@@ -2016,19 +2009,17 @@ int occupancy_exact(int M, int bf16) {
     return n;
 }
 
-int occupancy_refine(int M, int bf16) {
+int occupancy_batched(int M, int bf16, bool optional_stages) {
     int n = 0;
-    TSENOR_DISPATCH(M, bf16,
-                    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, refine_kernel<MM, B>,
-                                                                       kWave, 0));
-    return n;
-}
-
-int occupancy_batched(int M, int bf16) {
-    int n = 0;
-    TSENOR_DISPATCH(M, bf16,
-                    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, batched_kernel<MM, B>,
-                                                                       kWave, 0));
+    if (optional_stages) {
+        TSENOR_DISPATCH(M, bf16,
+                        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &n, batched_kernel<MM, B, true>, kWave, 0));
+    } else {
+        TSENOR_DISPATCH(M, bf16,
+                        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                            &n, batched_kernel<MM, B, false>, kWave, 0));
+    }
     return n;
 }
 
