@@ -318,6 +318,37 @@ def test_workload_every_block(name):
           flush=True)
 
 
+@pytest.mark.parametrize("name,block_rows", [
+    ("8:16-4096x11008-bf16", None),          # every block
+    ("16:32-8192x28672-bf16", (0, 1, 97, 128, 200, 255)),
+])
+def test_workload_polish(name, block_rows):
+    """The optional 2-opt polish (8 swaps per block) at workload size, in the
+    launch the benchmark's --polish-steps 8 line times: masks equal to the
+    oracle's rounding with the same polish of the GPU's S (on every block, or
+    on the listed block-rows), every block feasible."""
+    import torch
+    w, W_np, Wf = _workload(name)
+    K = 8
+    _note(w.name, f"polish {K}", "every block" if block_rows is None else f"block-rows {block_rows}")
+    W = to_device(W_np)
+    mask_t, S_t = sms.mask(W, w.N, w.M, w.tau, w.iters, w.ls_steps, return_frac=True,
+                           polish_steps=K)
+    torch.cuda.synchronize()
+    mask = words(mask_t)
+    assert_feasible(mask, w.rows, w.cols, w.N, w.M)
+    rows = range(w.rows // w.M) if block_rows is None else block_rows
+    swaps = 0
+    for br in ([None] if block_rows is None else rows):
+        sl = slice(None) if br is None else slice(br * w.M, (br + 1) * w.M)
+        S = S_t[sl].cpu().numpy()
+        ref, st = oracle.round_matrix_ex(S, np.ascontiguousarray(Wf[sl]), w.N, w.M, w.ls_steps, K)
+        assert np.array_equal(mask[sl], ref), f"block-row {br}"
+        swaps += int(st[4])
+    assert swaps > 0
+    print(f"{w.name} polish {K}: masks equal to the oracle's, {swaps} swaps", flush=True)
+
+
 def test_model7b_layer_batched():
     """One batched call over a 7B-shaped layer (8:16 attention, 16:32 MLP)
     equals per-matrix calls bit for bit; for every projection, every block's
