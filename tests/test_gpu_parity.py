@@ -6,9 +6,11 @@ fp64 oracle; masks bit-exact with the oracle's rounding applied to the GPU's S,
 and with the GPU's own rounding-only entry point on that S; every block
 feasible (N ones per row and column).  Small cases span several groups, a
 ragged last group and a partial last mask word; the workload-sized cases check
-sampled blocks (S) and whole block-rows (masks) at full size, in the launch
-configuration the benchmark times.
+every block (the 2-opt polish at 16:32: whole sampled block-rows) at full size,
+in the launch configuration the benchmark times.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -169,6 +171,10 @@ def test_power_of_two_scale_invariance(M, bf16, k):
     assert np.array_equal(S1, S2)
 
 
+# cases per seed of the random tests (TSENOR_RANDOM_CASES raises it for a long sweep)
+RANDOM_CASES = int(os.environ.get("TSENOR_RANDOM_CASES", "40"))
+
+
 @pytest.mark.parametrize("seed", [11, 12, 13])
 def test_random_configurations(seed):
     """Seeded random mixes of M, N (1..M), value distribution, tau (0..150),
@@ -177,7 +183,7 @@ def test_random_configurations(seed):
     the GPU's S, for the fused path and the rounding-only entry point."""
     import torch
     rng = np.random.default_rng(seed)
-    for case in range(40):
+    for case in range(RANDOM_CASES):
         M = int(rng.choice([4, 8, 16, 32]))
         N = int(rng.integers(1, M + 1))
         nbc, nbr = int(rng.integers(1, 12)), int(rng.integers(1, 3))
@@ -197,6 +203,46 @@ def test_random_configurations(seed):
         assert np.abs(S - S64).max() < S_TOL
         ref, _ = oracle.round_matrix(S, Wf, N, M, L)
         assert np.array_equal(mask, ref) and np.array_equal(mask2, ref)
+        assert_feasible(mask, *W.shape, N, M)
+
+
+@pytest.mark.parametrize("seed", [21, 22, 23])
+def test_random_configurations_optional_stages(seed):
+    """The random mixes above with the optional stages: 0..50 polish swaps and,
+    in a third of the cases, a previous mask (a shorter solve of the same W,
+    polished): masks bit-exact with the oracle's rounding with the same stages
+    of the GPU's S, every block feasible."""
+    import torch
+    rng = np.random.default_rng(seed)
+    for case in range(RANDOM_CASES):
+        M = int(rng.choice([4, 8, 16, 32]))
+        N = int(rng.integers(1, M + 1))
+        nbc, nbr = int(rng.integers(1, 12)), int(rng.integers(1, 3))
+        kind = str(rng.choice(["normal", "outlier", "student_t", "ties", "uniform"]))
+        tau = float(rng.choice([0.0, 5.0, 20.0, 60.0, 150.0]))
+        T = int(rng.choice([1, 2, 5, 20, 80]))
+        L = int(rng.choice([0, 1, 3, 8, 64]))
+        bf16 = bool(rng.integers(0, 2))
+        K = int(rng.choice([0, 1, 4, 50]))
+        use_prev = bool(rng.integers(0, 3) == 0)
+        W = np.concatenate([wl.random_blocks(seed * 10000 + 100 * case + r, nbc, M, kind)
+                            for r in range(nbr)]).astype(np.float32)
+        Wn = wl.f32_to_bf16_bits(W) if bf16 else W
+        _note(f"random stages seed={seed} case={case}: M={M} N={N} {W.shape} {kind} "
+              f"tau={tau} T={T} L={L} bf16={bf16} K={K} prev={use_prev}")
+        Wd = to_device(Wn)
+        prev = None
+        if use_prev:
+            prev = sms.mask(Wd, N, M, tau, max(1, T // 2), L, polish_steps=3)[0].clone()
+        m_t, S_t = sms.mask(Wd, N, M, tau, T, L, return_frac=True, polish_steps=K,
+                            prev_mask=prev)
+        torch.cuda.synchronize()
+        S = S_t.cpu().numpy()
+        mask = words(m_t)
+        Wf = as_f32(Wn)
+        ref, _ = oracle.round_matrix_ex(S, Wf, N, M, L, K,
+                                        words(prev) if prev is not None else None)
+        assert np.array_equal(mask, ref)
         assert_feasible(mask, *W.shape, N, M)
 
 
