@@ -364,7 +364,9 @@ def main():
                      "unit": "Tops/s", "frac": round(achieved / PEAK_VALU_TOPS, 4),
                      "traffic": measured_traffic(w.name) if args.polish_steps == 0 else None,
                      "kernel": "mask_kernel (gather + Dykstra + rounding + pack, one launch)"
-                               + (" + refine_kernel" if args.polish_steps else ""),
+                               if args.polish_steps == 0 else
+                               "mask_kernel with the optional stages (gather + Dykstra + rounding"
+                               " + 2-opt polish + pack, one launch)",
                      "kernel_ms": round(ms, 4),
                      "ops_per_launch": ops,
                      "hbm_algorithmic_bytes": hbm_bytes,
