@@ -40,14 +40,14 @@ KERNEL_SOURCE = os.path.join(ROOT, "sparse_mask_search_amd", "csrc", "tsenor_ker
 # dispatch scaled by what the same counters read for a 1 GiB device copy (x 2.0
 # read, x 1.0 written), valid only for the kernel source they were taken on.  The
 # 7B-shaped model's entry sums its two launches.
-TRAFFIC_SHA = "11a216a91fbda252df95f4ed9f2c21b666efa63a481ebc0397ff64f8921a85f1"
+TRAFFIC_SHA = "350b215cb332f40b8e8a6485d46117fb68c96357a67bcf13c549b74723d25531"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) in KiB per launch
-    "16:32-8192x28672-bf16": (952079.75, 965341.921875),
-    "16:32-8192x28672-bf16-tau200": (2511417.4375, 6678899.296875),
-    "8:16-4096x11008-bf16": (169909.25, 182700.109375),
-    "4:8-4096x4096-f32": (97053.375, 67901.375),
-    "2:4-1024x1024-f32": (2135.96875, 256.0),
-    "7b-model-batched": (17388834.5625 + 7873486.34375, 17572787.625 + 8517760.265625),
+    "16:32-8192x28672-bf16": (953632.0625, 965791.296875),
+    "16:32-8192x28672-bf16-tau200": (2496792.25, 952899.265625),
+    "8:16-4096x11008-bf16": (170159.90625, 182614.796875),
+    "4:8-4096x4096-f32": (96987.1875, 67871.15625),
+    "2:4-1024x1024-f32": (2139.15625, 256.0),
+    "7b-model-batched": (17372296.78125 + 7892737.0, 17574156.625 + 8519256.96875),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 

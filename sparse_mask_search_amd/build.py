@@ -24,11 +24,15 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
+def _flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp]
+    cmd = [hipcc()] + _flags() + ["-fPIC", "-shared", "-o", tmp]
     cmd += ["-x", "hip"] + [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         cmd.append("-Rpass-analysis=kernel-resource-usage")
@@ -36,6 +40,14 @@ def build(verbose: bool = False) -> str:
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
     return LIB
+
+
+def device_asm(source: str, out: str) -> str:
+    """gfx950 assembly of one HIP source, compiled as for the library."""
+    cmd = [hipcc()] + _flags() + ["--cuda-device-only", "-S", "-o", out,
+                                  os.path.join(CSRC, source)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out
 
 
 if __name__ == "__main__":
