@@ -40,14 +40,14 @@ KERNEL_SOURCE = os.path.join(ROOT, "sparse_mask_search_amd", "csrc", "tsenor_ker
 # dispatch scaled by what the same counters read for a 1 GiB device copy (x 2.0
 # read, x 1.0 written), valid only for the kernel source they were taken on.  The
 # 7B-shaped model's entry sums its two launches.
-TRAFFIC_SHA = "350b215cb332f40b8e8a6485d46117fb68c96357a67bcf13c549b74723d25531"
+TRAFFIC_SHA = "7e5a34058378bf0679dcdbf3f2ec78a0f56158160fb9693b6267596d3989b27e"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) in KiB per launch
-    "16:32-8192x28672-bf16": (953632.0625, 965791.296875),
-    "16:32-8192x28672-bf16-tau200": (2496792.25, 952899.265625),
-    "8:16-4096x11008-bf16": (170159.90625, 182614.796875),
-    "4:8-4096x4096-f32": (96987.1875, 67871.15625),
-    "2:4-1024x1024-f32": (2139.15625, 256.0),
-    "7b-model-batched": (17372296.78125 + 7892737.0, 17574156.625 + 8519256.96875),
+    "16:32-8192x28672-bf16": (470809.21875, 38838.625),
+    "16:32-8192x28672-bf16-tau200": (1995094.25, 48058.828125),
+    "8:16-4096x11008-bf16": (74973.28125, 5504.046875),
+    "4:8-4096x4096-f32": (52681.8125, 3072.0),
+    "2:4-1024x1024-f32": (2140.15625, 256.0),
+    "7b-model-batched": (8689485.1875 + 4177922.78125, 582410.65625 + 262144.0),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 

@@ -50,10 +50,13 @@
  *     their W (and S) on the device, wait for the count, and return
  *     TSENOR_ERR_NONFINITE without launching anything else if it is not zero.
  *     The wait synchronises `stream`, so such calls cannot be graph-captured.
- *   - The library keeps one cached device workspace per device (allocated on
- *     first use, grown on demand, never freed before process exit).  Calls on
- *     one device share it: each launch is ordered after the previous one on
- *     the device (stream event), so concurrent calls from any thread or
+ *   - The kernels need no device workspace: every intermediate of the path
+ *     lives in registers and LDS.  The library keeps a few cached buffers per
+ *     device (the batched descriptor table, a copy of a previous mask that
+ *     overlaps an output; allocated on first use, grown on demand, never
+ *     freed before process exit).  Calls on one device other than
+ *     tsenor_mask_noalloc are ordered: each launch follows the previous one
+ *     on the device (stream event), so concurrent calls from any thread or
  *     stream are safe but do not overlap.  The host side is thread-safe.
  */
 #ifndef TSENOR_H
@@ -122,17 +125,13 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
  * arguments, result (bit-identical masks and S) and argument errors as
  * tsenor_mask.  It calls no hipMalloc, hipFree or other allocating routine and
- * records or waits on no event: its workspace is a fixed 64 MiB array in
- * device memory, one copy per GPU, present from the library's first kernel
- * launch on that GPU until the process ends.  The launch grid is capped at the
- * array's workgroup slots (on a 256-CU MI355X every M runs its full grid), so
- * no matrix size is beyond it.  Nothing in the array needs clearing between
- * calls (every slot is written before it is read).  Calls of this entry point
- * on one GPU share the array: two that overlap in time (different streams, or
- * threads without ordering) race and give undefined results; calls on one
- * stream are ordered.  It does not share the workspace of the other entry
- * points, so it may overlap them.  TSENOR_DEBUG_CHECKS is ignored here (its
- * check allocates).  The first call on a device also reads the device's
+ * records or waits on no event.  The path needs no workspace (every
+ * intermediate lives in registers and LDS), so no matrix size is beyond it,
+ * nothing needs clearing between calls, and calls that overlap in time
+ * (different streams, threads without ordering) are independent as long as
+ * their outputs do not overlap.  It is not ordered after the other entry
+ * points' launches.  TSENOR_DEBUG_CHECKS is ignored here (its check
+ * allocates).  The first call on a device also reads the device's
  * launch geometry (CU count, kernel occupancies).                             */
 int tsenor_mask_noalloc(const void* W, int dtype, int64_t rows, int64_t cols, int64_t ld,
                         int N, int M, float tau, int iters, int ls_steps, uint32_t* mask_out,

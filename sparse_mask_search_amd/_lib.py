@@ -162,8 +162,8 @@ def mask(W, N: int, M: int, tau: float, iters: int, ls_steps: int, return_frac: 
 def mask_noalloc(W, N: int, M: int, tau: float, iters: int, ls_steps: int, out, frac_out=None,
                  stream=None):
     """tsenor_mask_noalloc: the mask of W into the caller's `out` (and S into
-    `frac_out` when given), with the library allocating nothing (its
-    workspace is a fixed device array).  Overlapping calls on one GPU race."""
+    `frac_out` when given), with the library allocating nothing and recording
+    no event (the path needs no workspace)."""
     dt = _weights(W)
     rows, cols = W.shape
     if out is None:

@@ -1,8 +1,8 @@
 // tsenor_abi.cpp -- the extern "C" boundary declared in include/tsenor.h.
 //
 // Host-side only: argument validation (before any HIP call), the per-device
-// workspace cache, launch geometry, and the stream ordering that makes the
-// shared workspace safe.  The arithmetic of the method lives entirely in the
+// cached buffers (batched descriptor table, previous-mask copy), launch
+// geometry, and the stream ordering that makes the shared buffers safe.  The arithmetic of the method lives entirely in the
 // kernels (tsenor_kernels.hip).
 #include <hip/hip_runtime.h>
 
@@ -19,15 +19,6 @@
 
 using tsenor::MatJob;
 using tsenor::Params;
-
-// Workspace of tsenor_mask_noalloc: a fixed array in device memory, one copy
-// per GPU, for callers that cannot allocate.  Host code reaches it only
-// through the address hipGetSymbolAddress returns per device (the name
-// itself is a host-side stand-in).  16 Mi floats (64 MiB) hold one workspace
-// slot per workgroup of a full persistent grid on a 256-CU device for every M
-// (M = 8 and 32 need the most: 4096 slots of 16 KiB, 2048 of 32 KiB).
-constexpr size_t kFixedScratchFloats = size_t(16) << 20;
-static __device__ __align__(256) float scratch[kFixedScratchFloats];
 
 namespace {
 
@@ -49,8 +40,6 @@ struct DeviceState {
     bool init = false;              // num_cu and the occupancy tables
     bool ordered = false;           // `last` exists
     int num_cu = 0;
-    float* scratch = nullptr;
-    size_t scratch_floats = 0;
     hipEvent_t last = nullptr;      // completion of the newest launch that used this state
     MatJob* jobs_dev = nullptr;     // batched descriptor table (device)
     MatJob* jobs_host[kStageRing] = {};   // pinned staging copies, used in turn
@@ -67,7 +56,6 @@ struct DeviceState {
     size_t prev_cap = 0;            // words
     int* dbg_count = nullptr;       // debug checks: device counter and its pinned host copy
     int* dbg_host = nullptr;
-    float* fixed_scratch = nullptr; // device address of this GPU's copy of `scratch` (below)
 };
 DeviceState g_dev[kMaxDevices];
 
@@ -144,16 +132,16 @@ int acquire_geometry(DeviceState** out, std::unique_lock<std::mutex>* lk) {
 }
 
 // Flags of the library's internal events.  They only order work on one
-// device (launches sharing the workspace, uploads from a staging buffer) and
-// let the host wait for completion before reusing or freeing a buffer;
+// device (launches sharing the cached buffers, uploads from a staging buffer)
+// and let the host wait for completion before reusing or freeing a buffer;
 // nothing reads device memory through them, so they skip the system-scope
 // cache writeback and invalidation that a default event performs at every
-// record (measured: 5 us per 2:4 call, 29 us per 4:8 call whose workspace
-// holds 64 MB of dirty lines).
+// record (measured: 5 us per 2:4 call, 29 us per 4:8 call that had left 64 MB
+// of dirty lines).
 constexpr unsigned kEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
 
 // acquire_geometry, plus the event that orders the launches sharing the
-// cached workspace.
+// cached buffers.
 int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
     int code = acquire_geometry(out, lk);
     if (code != TSENOR_OK) return code;
@@ -163,28 +151,6 @@ int acquire(DeviceState** out, std::unique_lock<std::mutex>* lk) {
         if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
         st.ordered = true;
     }
-    return TSENOR_OK;
-}
-
-// Ensure the workspace holds `floats` floats.  Growing waits for every
-// earlier launch that may still read the old buffer.
-int ensure_scratch(DeviceState& st, size_t floats) {
-    if (st.scratch_floats >= floats) return TSENOR_OK;
-    hipError_t e;
-    if (st.scratch != nullptr) {
-        e = hipEventSynchronize(st.last);
-        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
-        e = hipFree(st.scratch);
-        if (e != hipSuccess) return hip_fail(e, "hipFree");
-        st.scratch = nullptr;
-        st.scratch_floats = 0;
-    }
-    e = hipMalloc(&st.scratch, floats * sizeof(float));
-    if (e != hipSuccess) {
-        st.scratch = nullptr;
-        return hip_fail(e, "hipMalloc(workspace)");
-    }
-    st.scratch_floats = floats;
     return TSENOR_OK;
 }
 
@@ -304,14 +270,11 @@ int tsenor_mask_ex(const void* W, int dtype, int64_t rows, int64_t cols, int64_t
     const int64_t grid = clamp_grid(
         groups_of(job), st->num_cu,
         optional ? st->occ_mask_opt[job.bf16][M] : st->occ_mask[job.bf16][M]);
-    if ((st_code = ensure_scratch(*st, (size_t)grid * (size_t)tsenor::slot_floats(M))) != TSENOR_OK)
-        return st_code;
     Params prm;
     prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
     prm.iters = iters;
     prm.ls_steps = ls_steps;
     prm.polish_steps = polish_steps;
-    prm.scratch = st->scratch;
     const size_t words = (size_t)rows * (size_t)job.wpr;
     // a previous mask that the solve overwrites (any overlap with the output)
     // is copied first
@@ -341,33 +304,16 @@ int tsenor_mask_noalloc(const void* W, int dtype, int64_t rows, int64_t cols, in
     if (st_code != TSENOR_OK) return st_code;
     st_code = check_params(tau, iters, ls_steps);
     if (st_code != TSENOR_OK) return st_code;
-    const size_t slot = (size_t)tsenor::slot_floats(M);
-    if (slot == 0 || slot > kFixedScratchFloats) return TSENOR_ERR_NM;
-
     DeviceState* st = nullptr;
     std::unique_lock<std::mutex> lk;
     if ((st_code = acquire_geometry(&st, &lk)) != TSENOR_OK) return st_code;
-    if (st->fixed_scratch == nullptr) {
-        // once per device, with that device current: this GPU's copy of the array
-        void* ptr = nullptr;
-        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
-        if (e != hipSuccess || ptr == nullptr)
-            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
-        st->fixed_scratch = static_cast<float*>(ptr);
-    }
     MatJob job = make_job(W, dtype, rows, cols, ld, N, M, mask_out, frac_out);
-    // The kernel's grid is persistent (workgroups stride over the groups), so
-    // any matrix runs in any grid: the grid is the usual one, capped at the
-    // number of workgroup slots the array holds.
-    int64_t grid = clamp_grid(groups_of(job), st->num_cu, st->occ_mask[job.bf16][M]);
-    const int64_t cap = (int64_t)(kFixedScratchFloats / slot);
-    if (grid > cap) grid = cap;
+    const int64_t grid = clamp_grid(groups_of(job), st->num_cu, st->occ_mask[job.bf16][M]);
     Params prm;
     prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
     prm.iters = iters;
     prm.ls_steps = ls_steps;
     prm.polish_steps = 0;
-    prm.scratch = st->fixed_scratch;
     hipError_t e = (hipError_t)tsenor::launch_mask(job, prm, (int)grid, stream);
     return e == hipSuccess ? TSENOR_OK : hip_fail(e, "mask kernel launch");
 }
@@ -561,7 +507,6 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
     struct Class { int M, bf16, first, n; int64_t groups, grid; };
     Class cls[8];
     int ncls = 0, filled = 0;
-    int64_t max_floats = 0;
     for (int M : {32, 16, 8, 4})
         for (int b = 0; b < 2; ++b) {
             Class c{M, b, filled, 0, 0, 0};
@@ -579,17 +524,13 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
             if (c.n == 0) continue;
             c.grid = clamp_grid(c.groups, st->num_cu,
                                 optional ? st->occ_batched_opt[b][M] : st->occ_batched[b][M]);
-            const int64_t need = c.grid * tsenor::slot_floats(M);
-            max_floats = need > max_floats ? need : max_floats;
             cls[ncls++] = c;
         }
-    if ((st_code = ensure_scratch(*st, (size_t)max_floats)) != TSENOR_OK) return st_code;
     Params prm;
     prm.tau_log2e = (float)((double)tau * 1.4426950408889634);
     prm.iters = iters;
     prm.ls_steps = ls_steps;
     prm.polish_steps = polish_steps;
-    prm.scratch = st->scratch;
     if ((st_code = order_and_record_begin(*st, s)) != TSENOR_OK) return st_code;
     e = hipMemcpyAsync(st->jobs_dev, table, sizeof(MatJob) * (size_t)count,
                        hipMemcpyHostToDevice, s);
@@ -606,13 +547,13 @@ int tsenor_mask_batched_ex(const tsenor_matrix* mats, int count, float tau, int 
             return hip_fail(e, "hipMemcpyAsync(previous mask)");
         }
     }
-    // The launches run in stream order, so they share the workspace.
+    // The launches run in stream order after the descriptor upload.
     for (int k = 0; k < ncls; ++k) {
         const Class& c = cls[k];
         e = (hipError_t)tsenor::launch_batched(st->jobs_dev + c.first, c.n, c.groups, c.M, c.bf16,
                                                prm, optional, (int)c.grid, stream);
         if (e != hipSuccess) {
-            // earlier classes may be in flight: keep the workspace ordering
+            // earlier classes may be in flight: keep the ordering
             (void)record_end(*st, s);
             return hip_fail(e, "batched kernel launch");
         }

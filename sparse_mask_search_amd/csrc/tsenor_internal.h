@@ -24,7 +24,6 @@ struct Params {
     int32_t iters;
     int32_t ls_steps;
     int32_t polish_steps;  // optional 2-opt swaps per block (0: none)
-    float* scratch;     // one slot of slot_floats(M) floats per workgroup
 };
 
 // Work decomposition: one workgroup = one wave (64 lanes) processes a "group"
@@ -34,10 +33,6 @@ constexpr int kWave = 64;
 // Blocks per group of the fused kernel for pattern size M (the solve layout
 // is fixed per M in tsenor_kernels.hip).
 int blocks_per_group(int M);
-// Floats of workspace one workgroup of the fused kernels uses for pattern
-// size M: the fractional S of its group, blocks_per_group(M) * M * M (4, 16,
-// 16 and 32 KiB for M = 4, 8, 16, 32); 0 for an unsupported M.
-int64_t slot_floats(int M);
 
 // Host-side launchers (tsenor_kernels.hip).  They return a hipError_t value.
 // The fused kernel runs the optional stages -- at most prm.polish_steps 2-opt

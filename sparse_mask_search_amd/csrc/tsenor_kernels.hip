@@ -26,9 +26,14 @@
 //              spread over several lanes meet in a DPP butterfly
 //              (reduce-scatter, per-owner update of V), and the owners' new
 //              V goes back to every lane through LDS.
-//  3. export   S = min(P V U, 1) is written to the workgroup's scratch slot
-//              (and to frac_out when asked).
-//  4. round    blocks are re-read from the slot one row and one column per
+//  3. export   M >= 8: each block's record -- its log2 row and column offsets
+//              with the final scales folded in, and its score scale -- goes
+//              to LDS, from which S = min(P V U, 1) = min(2^(scale |W| +
+//              row + col), 1) is rebuilt row by row with |W| (read again)
+//              by the rounding, which also writes frac_out when asked; S
+//              never goes to memory.  M = 4: S itself goes to the LDS
+//              staging of the rounding.
+//  4. round    blocks are staged in LDS one row and one column per
 //              lane.  The greedy over the (S desc, index asc) order is computed
 //              as its equivalent fixed point: accepted = {key >= phi_i and
 //              key >= theta_j} where phi_i / theta_j is the N-th largest key
@@ -99,8 +104,6 @@ template <int M> constexpr int kSwzG1 = 0x1F | (((M == 32) ? 7 : 2) << 10);
 constexpr int kSwzG0 = 0x1F | (1 << 10);
 static_assert(kCW<32> == 16 && kG<32> == 4 && kH<32> == 2, "the butterfly's tile shape");
 static_assert(kCW<16> == 16 && kG<16> == 4 && kH<16> == 1, "the butterfly's tile shape");
-// Workspace of one workgroup: the S of its group's blocks, row-major per block.
-template <int M> constexpr int64_t kSlot = (int64_t)kBPG<M> * M * M;
 // Blocks whose cycle-1 kernel reaches below 2^kDeepLog2 rescale in log2 space.
 // fp32 emulation of the iteration against the fp64 oracle: folding in the
 // linear domain stays within 5e-6 while the minimum is above ~-115 and fails
@@ -129,8 +132,8 @@ template <int M> constexpr int kStageRow = (M == 4) ? 4 : M + 4;
 template <int M> constexpr int kStageBlk = (M == 4) ? 16 : M * (M + 4) + (M < 32 ? M : 0);
 // Blocks the staging area holds: one rounding pass (64 / M blocks), except
 // for M = 4, where the solve exports the S of its whole group (32 blocks, two
-// passes) straight into LDS instead of the workspace slot: small blocks give
-// a wave too little work to hide the slot's round trip through memory.
+// passes) straight into LDS; larger M rebuild S pass by pass from per-block
+// records (kRec) instead.
 template <int M> constexpr bool kStageInLds = (M == 4);
 template <int M> constexpr int kStaged = kStageInLds<M> ? kBPG<M> : kWave / M;
 // |W| for the local search follows the staging area: block q, row i at
@@ -138,9 +141,23 @@ template <int M> constexpr int kStaged = kStageInLds<M> ? kBPG<M> : kWave / M;
 template <int M> constexpr int rnd_lds_floats() {
     return kStaged<M> * kStageBlk<M> + (kWave / M) * M * (M + 1) + kWave;
 }
-template <int M> constexpr int lds_floats() {
+template <int M> constexpr int solve_round_floats() {
     return dyk_lds_floats<M>() > rnd_lds_floats<M>() ? dyk_lds_floats<M>() : rnd_lds_floats<M>();
 }
+// M >= 8: the solve leaves a record of each block of the group for the
+// rounding, which rebuilds S from it and |W| instead of reading S back from
+// memory: the final log2 row offsets (M floats), column offsets (M) and the
+// score scale, S_ij = min(2^(scale |W_ij| + row_i + col_j), 1).  The records
+// follow the solve's and the rounding's areas and live from the end of the
+// solve to the end of the group's rounding.
+// Records of M >= 16 are padded to a multiple of 4 floats so that the column
+// offsets are read 16 bytes at a time; M = 8 keeps 2M + 1 (its 64 records
+// would otherwise push a workgroup's LDS past what four waves per SIMD allow).
+template <int M> constexpr int kRec = (M >= 16) ? 2 * M + 4 : 2 * M + 1;
+template <int M> constexpr int rec_floats() { return kStageInLds<M> ? 0 : kBPG<M> * kRec<M>; }
+template <int M> constexpr int lds_floats() { return solve_round_floats<M>() + rec_floats<M>(); }
+static_assert(solve_round_floats<32>() % 4 == 0 && solve_round_floats<16>() % 4 == 0,
+              "the records of M >= 16 start 16-byte aligned");
 
 template <int M> constexpr uint32_t kFull = (M == 32) ? 0xFFFFFFFFu : ((1u << M) - 1u);
 // Waves per SIMD the solve+round kernels are built for.  The register budget
@@ -155,7 +172,9 @@ __device__ __forceinline__ float rcpf(float x) { return __builtin_amdgcn_rcpf(x)
 
 // ---------------------------------------------------------------- gather
 // Native vector types for the streaming (non-temporal) loads of W: the
-// weights are read once and should not evict the workspace slots from L2.
+// weights stream through once per solve (the rounding reads a group's rows
+// again only after the group's solve), so they should not displace other
+// lines from L2.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -375,12 +394,12 @@ __device__ __forceinline__ void rnd_sync() {
 }
 
 // ---------------------------------------------------------------- solve
-// Dykstra for the group's blocks; writes S (fp32) for block b of the group to
-// slot[b*M*M ...] row-major, and to job.frac when requested.
+// Dykstra for the group's blocks.  M >= 8: leaves each block's record (see
+// kRec) in LDS for the rounding, which rebuilds S from it.  M = 4: writes S
+// into the rounding's LDS staging, and to job.frac when requested.
 template <int M, bool BF16>
 __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& prm, int64_t br,
-                                              int64_t bc0, float* __restrict__ slot,
-                                              float* __restrict__ lds) {
+                                              int64_t bc0, float* __restrict__ lds) {
     constexpr int R = kR<M>, H = kH<M>, CW = kCW<M>, L = kL<M>;
     // M = 32: an opaque lane, so that addresses derived from it are rebuilt
     // per group instead of being hoisted out of the kernel's group loop, where
@@ -404,12 +423,14 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
     const int64_t row0 = br * M + g * R;      // first matrix row of this lane's tile
     const int64_t col0 = bc * M + h * CW;     // first matrix column of this lane's tile
     // Lane's part of the LDS behind the column-scale exchange (free during
-    // the solve): a deep block's log2 row offsets (R), column offsets (CW)
-    // and score scale, entry k of the lane at k * kWave (see the rescaling
-    // below).
+    // the solve): the block's log2 row offsets (R), column offsets (CW) and
+    // score scale, entry k of the lane at k * kWave, so that log2 P = scale
+    // |W| + row offset + column offset holds through every rescaling below.
+    // Kept for every block at M >= 8 (the export's record is made from it),
+    // for deep blocks only at M = 4.
     float* offs = lds + dyk_lds_floats<M>() + lane;
-    static_assert(dyk_lds_floats<M>() + kWave * (R + CW + 1) <= lds_floats<M>(),
-                  "the deep blocks' offsets fit the LDS");
+    static_assert(dyk_lds_floats<M>() + kWave * (R + CW + 1) <= solve_round_floats<M>(),
+                  "the offsets fit the LDS");
 
     float P[R][CW];
 #pragma unroll
@@ -525,7 +546,7 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
 #pragma unroll
         for (int s = 1; s < L; s <<= 1) dflag |= __shfl_xor(dflag, s);
         deep = dflag != 0;
-        if (deep) {
+        if (!kStageInLds<M> || deep) {
 #pragma unroll
             for (int r = 0; r < R; ++r) offs[r * kWave] = rho[r];
 #pragma unroll
@@ -707,6 +728,15 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                         P[r][c] = ex2(fmaf(P[r][c], sc, ro) + of[(R + c) * kWave]);
                 }
             } else if (f) {
+                if constexpr (!kStageInLds<M>) {  // the offsets follow the fold
+                    int ln = threadIdx.x;
+                    asm volatile("" : "+v"(ln));
+                    float* of = lds + dyk_lds_floats<M>() + ln;
+#pragma unroll
+                    for (int c = 0; c < CW; ++c) of[(R + c) * kWave] += lg2(V[c]);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) of[r * kWave] += lg2(U[r]);
+                }
 #pragma unroll
                 for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -721,32 +751,48 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
         }
     }
 
-    // ---- export S = exp(X) = min(P U V, 1) ----
-    const bool fvec = ((reinterpret_cast<uintptr_t>(job.frac) & 15u) == 0);
+    if constexpr (kStageInLds<M>) {
+        // ---- export S = exp(X) = min(P U V, 1) into the rounding's staging ----
+        const bool fvec = ((reinterpret_cast<uintptr_t>(job.frac) & 15u) == 0);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        float s[CW];
+        for (int r = 0; r < R; ++r) {
+            float s[CW];
 #pragma unroll
-        for (int c = 0; c < CW; ++c) s[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
-        float* srow = kStageInLds<M>
-                          ? lds + blk * kStageBlk<M> + (g * R + (r ^ rsw)) * kStageRow<M> + h * CW
-                          : slot + blk * M * M + (g * R + (r ^ rsw)) * M + h * CW;
+            for (int c = 0; c < CW; ++c) s[c] = __builtin_amdgcn_fmed3f((P[r][c] * V[c]) * U[r], 0.0f, 1.0f);
+            float* srow = lds + blk * kStageBlk<M> + (g * R + (r ^ rsw)) * kStageRow<M> + h * CW;
 #pragma unroll
-        for (int q = 0; q < CW / 4; ++q)
-            *reinterpret_cast<float4*>(srow + 4 * (q ^ sw)) =
-                make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
-        if (job.frac != nullptr && valid) {
-            float* frow = job.frac + (row0 + (r ^ rsw)) * job.cols + col0;
-            if (fvec) {
+            for (int q = 0; q < CW / 4; ++q)
+                *reinterpret_cast<float4*>(srow + 4 * (q ^ sw)) =
+                    make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+            if (job.frac != nullptr && valid) {
+                float* frow = job.frac + (row0 + (r ^ rsw)) * job.cols + col0;
+                if (fvec) {
 #pragma unroll
-                for (int q = 0; q < CW / 4; ++q)
-                    *reinterpret_cast<float4*>(frow + 4 * (q ^ sw)) =
-                        make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
-            } else {
+                    for (int q = 0; q < CW / 4; ++q)
+                        *reinterpret_cast<float4*>(frow + 4 * (q ^ sw)) =
+                            make_float4(s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]);
+                } else {
 #pragma unroll
-                for (int c = 0; c < CW; ++c) frow[(c & 3) + 4 * ((c >> 2) ^ sw)] = s[c];
+                    for (int c = 0; c < CW; ++c) frow[(c & 3) + 4 * ((c >> 2) ^ sw)] = s[c];
+                }
             }
         }
+    } else {
+        // ---- the block's record: offsets with the final scales folded in ----
+        // S = min(P U V, 1) = min(2^(scale |W| + row + col), 1), rebuilt by the
+        // rounding.  Each row is written by the lanes of its h = 0 column half,
+        // each column by the lanes of row group 0, the scale by lane 0.
+        float* rb = lds + solve_round_floats<M>() + blk * kRec<M>;
+        if (H == 1 || h == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) rb[g * R + (r ^ rsw)] = offs[r * kWave] + lg2(U[r]);
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int c = 0; c < CW; ++c)
+                rb[M + h * CW + 4 * ((c >> 2) ^ sw) + (c & 3)] = offs[(R + c) * kWave] + lg2(V[c]);
+        }
+        if (lb == 0) rb[2 * M] = offs[(R + CW) * kWave];
     }
 }
 
@@ -1197,21 +1243,74 @@ __device__ __forceinline__ void load_pass_rows(const float* __restrict__ Sb, int
     }
 }
 
-// The next pass whose rows round_pass loads ahead (after its own rows are
+// Row i of |W| of a rounding pass's block (block column bc of block-row br);
+// zeros for a block past the matrix.
+template <int M, bool BF16>
+__device__ __forceinline__ void load_abs_pass_row(const MatJob& job, int64_t br, int64_t bc,
+                                                  bool valid, int i, float (&a)[M]) {
+    if (valid) {
+        load_abs_row<M, BF16>(job.W, (br * M + i) * job.ld + bc * M, job.aligned != 0, a);
+    } else {
+#pragma unroll
+        for (int j = 0; j < M; ++j) a[j] = 0.f;
+    }
+}
+
+// Row i of S of a rounding pass's block rebuilt from the block's record rb
+// (see kRec) and its row of |W|: S_ij = min(2^(scale |W_ij| + row_i +
+// col_j), 1), zeros for a block past the matrix.  The row is also the S
+// output when one is requested.
+template <int M>
+__device__ __forceinline__ void rebuild_row(const float* __restrict__ rb, const MatJob& job,
+                                            int64_t br, int64_t bc, bool valid, int i,
+                                            const float (&a)[M], float (&v)[M]) {
+    // Every record holds finite values (a block past the matrix solves a
+    // zero block), so the row is computed for every lane and then zeroed
+    // with one multiply: a conditional here became a branch per element.
+    float col[M];
+    if constexpr (kRec<M> % 4 == 0) {
+#pragma unroll
+        for (int q = 0; q < M / 4; ++q) {
+            const float4 c4 = *reinterpret_cast<const float4*>(rb + M + 4 * q);
+            col[4 * q] = c4.x; col[4 * q + 1] = c4.y; col[4 * q + 2] = c4.z; col[4 * q + 3] = c4.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < M; ++j) col[j] = rb[M + j];
+    }
+    const float sc = rb[2 * M], ro = rb[i];
+    const float keep = valid ? 1.0f : 0.0f;
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+        v[j] = __builtin_amdgcn_fmed3f(ex2(fmaf(a[j], sc, ro) + col[j]), 0.0f, 1.0f) * keep;
+    if (job.frac != nullptr && valid) {
+        float* frow = job.frac + (br * M + i) * job.cols + bc * M;
+        if ((reinterpret_cast<uintptr_t>(frow) & 15u) == 0) {
+#pragma unroll
+            for (int q = 0; q < M / 4; ++q)
+                *reinterpret_cast<float4*>(frow + 4 * q) =
+                    make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < M; ++j) frow[j] = v[j];
+        }
+    }
+}
+
+// The next pass whose |W| rows round_pass loads ahead (after its own rows are
 // staged), so that their memory latency overlaps this pass's sorts and greedy.
 // Used at M = 8 (eight passes per group; 1-3% faster at 4:8 and 8:16 in A/B
-// runs); at M = 32 the 64 registers it holds through the rounding made the
-// 16:32 launch 2% slower, and at M = 16 it measured the same as none.
+// runs); at M = 32 the registers it holds through the rounding made the 16:32
+// launch 2% slower, and at M = 16 it measured the same as none.
 template <int M> constexpr bool kPrefetch = (M == 8);
 struct NextPass {
-    const float* Sb;
-    int64_t sld, bc;
+    int64_t bc;
     bool valid, any;
 };
 
 // How a rounding pass gets its rows: loaded here from Sb (row stride sld) and
 // W; given by the caller (v = S, a = |W|), optionally loading the next pass's
-// rows ahead into vn, an; or S already in the LDS staging at Ss and a given.
+// |W| rows ahead into an; or S already in the LDS staging at Ss and a given.
 enum RowSource { kRowsLoad = 0, kRowsGiven = 1, kRowsStaged = 2 };
 
 // Rounding of the 64/M blocks of one pass; lane (q, i) = block q, row i.
@@ -1223,7 +1322,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
                                            const MatJob& job, int64_t br, int64_t bc, bool valid,
                                            int ls_steps, float* __restrict__ Ss,
                                            float* __restrict__ lds, const NextPass& nx,
-                                           float (&vn)[M], float (&an)[M],
+                                           float (&an)[M],
                                            int polish_steps = 0) {
     constexpr int G = kWave / M;
     constexpr uint32_t FULL = kFull<M>;
@@ -1262,7 +1361,7 @@ __device__ __forceinline__ void round_pass(const float* __restrict__ Sb, int64_t
     }
     rnd_sync<M>();
     if constexpr (SRC == kRowsGiven) {
-        if (nx.any) load_pass_rows<M, BF16>(nx.Sb, nx.sld, job, br, nx.bc, nx.valid, i, vn, an);
+        if (nx.any) load_abs_pass_row<M, BF16>(job, br, nx.bc, nx.valid, i, an);
     }
     uint32_t rpb[M], cpb[M];
     // An opaque zero in the keys' low words: with compile-time constants there
@@ -1755,7 +1854,7 @@ __global__ __launch_bounds__(kWave) void exact_kernel(MatJob job, const uint32_t
 // Whole path for group gl (block-row br, first block column bc0) of one matrix.
 template <int M, bool BF16, bool POLISH>
 __device__ __forceinline__ void process_group(const MatJob& job, const Params& prm, int64_t gl,
-                                              float* slot, float* lds) {
+                                              float* lds) {
     constexpr int BPG = kBPG<M>, G = kWave / M;
     const int64_t nbc = job.cols / M;
     const int64_t gpr = (nbc + BPG - 1) / BPG;
@@ -1782,10 +1881,10 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
 #pragma unroll
         for (int j = 0; j < M; ++j) apre[0][j] = 0.f;
     }
-    dykstra_group<M, BF16>(job, prm, br, bc0, slot, lds);
-    __syncthreads();  // S stores visible to every lane; LDS free for rounding
+    dykstra_group<M, BF16>(job, prm, br, bc0, lds);
+    __syncthreads();  // S or the records visible to every lane; LDS free for rounding
     set_prio<kPrioRound>();
-    const NextPass none{nullptr, 0, 0, false, false};
+    const NextPass none{0, false, false};
     if constexpr (kStageInLds<M>) {
         float unused[M];
 #pragma unroll
@@ -1794,40 +1893,44 @@ __device__ __forceinline__ void process_group(const MatJob& job, const Params& p
             round_pass<M, BF16, kRowsStaged, POLISH>(nullptr, 0, apre[p], apre[p], job, br, bc,
                                                      bc < nbc, prm.ls_steps,
                                                      lds + p * G * kStageBlk<M>, lds, none,
-                                                     unused, unused, prm.polish_steps);
+                                                     unused, prm.polish_steps);
             __syncthreads();
         }
     } else {
-        // kPrefetch: pass p + 1's rows are loaded during pass p (in round_pass,
-        // after staging).  An opaque lane keeps the row addresses from being
-        // hoisted out of the kernel's group loop (and held through the solve).
-        float v[M], a[M], vn[M], an[M];
+        // Each pass's rows of S are rebuilt from the blocks' records and |W|.
+        // kPrefetch: pass p + 1's |W| rows are loaded during pass p (in
+        // round_pass, after staging).  An opaque lane keeps the row addresses
+        // from being hoisted out of the kernel's group loop (and held through
+        // the solve).
+        const float* rec = lds + solve_round_floats<M>();
+        float v[M], a[M], an[M];
+        int lane = (int)threadIdx.x;
+        asm volatile("" : "+v"(lane));
+        const int q = lane / M, i = lane % M;
         if constexpr (kPrefetch<M>) {
-            int lane = (int)threadIdx.x;
-            asm volatile("" : "+v"(lane));
-            const int q = lane / M, i = lane % M;
-            load_pass_rows<M, BF16>(slot + q * M * M, M, job, br, bc0 + q, bc0 + q < nbc, i, v,
-                                    a);
+            load_abs_pass_row<M, BF16>(job, br, bc0 + q, bc0 + q < nbc, i, a);
 #pragma unroll 1
             for (int p = 0; p < PASSES; ++p) {
                 const int64_t bc = bc0 + p * G + q, bcn = bc + G;
-                const NextPass nx{slot + ((p + 1) * G + q) * M * M, M, bcn, bcn < nbc,
-                                  p + 1 < PASSES};
+                rebuild_row<M>(rec + (p * G + q) * kRec<M>, job, br, bc, bc < nbc, i, a, v);
+                const NextPass nx{bcn, bcn < nbc, p + 1 < PASSES};
                 round_pass<M, BF16, kRowsGiven, POLISH>(nullptr, 0, v, a, job, br, bc, bc < nbc,
-                                                        prm.ls_steps, lds, lds, nx, vn, an,
+                                                        prm.ls_steps, lds, lds, nx, an,
                                                         prm.polish_steps);
                 __syncthreads();
 #pragma unroll
-                for (int j = 0; j < M; ++j) { v[j] = vn[j]; a[j] = an[j]; }
+                for (int j = 0; j < M; ++j) a[j] = an[j];
             }
         } else {
 #pragma unroll 1
             for (int p = 0; p < PASSES; ++p) {
-                const int lb = p * G + (int)threadIdx.x / M;
+                const int lb = p * G + q;
                 const int64_t bc = bc0 + lb;
-                round_pass<M, BF16, kRowsLoad, POLISH>(slot + lb * M * M, M, v, a, job, br, bc,
-                                                       bc < nbc, prm.ls_steps, lds, lds, none,
-                                                       vn, an, prm.polish_steps);
+                load_abs_pass_row<M, BF16>(job, br, bc, bc < nbc, i, a);
+                rebuild_row<M>(rec + lb * kRec<M>, job, br, bc, bc < nbc, i, a, v);
+                round_pass<M, BF16, kRowsGiven, POLISH>(nullptr, 0, v, a, job, br, bc, bc < nbc,
+                                                        prm.ls_steps, lds, lds, none, an,
+                                                        prm.polish_steps);
                 __syncthreads();
             }
         }
@@ -1842,9 +1945,8 @@ void mask_kernel(MatJob job, Params prm) {
     constexpr int BPG = kBPG<M>;
     const int64_t nbc = job.cols / M;
     const int64_t ngroups = (job.rows / M) * ((nbc + BPG - 1) / BPG);
-    float* slot = prm.scratch + (int64_t)blockIdx.x * kSlot<M>;
     for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x)
-        process_group<M, BF16, POLISH>(job, prm, g, slot, lds);
+        process_group<M, BF16, POLISH>(job, prm, g, lds);
 }
 
 template <int M, bool BF16>
@@ -1855,7 +1957,7 @@ __global__ __launch_bounds__(kWave) void round_kernel(MatJob job, const float* _
     const int64_t nbc = job.cols / M;
     const int64_t gpr = (nbc + G - 1) / G;
     const int64_t ngroups = (job.rows / M) * gpr;
-    const NextPass none{nullptr, 0, 0, false, false};
+    const NextPass none{0, false, false};
     float unused[M];
     for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
         const int64_t br = g / gpr;
@@ -1863,7 +1965,7 @@ __global__ __launch_bounds__(kWave) void round_kernel(MatJob job, const float* _
         const bool valid = bc < nbc;
         const float* Sb = S + br * M * sld + (valid ? bc : 0) * M;
         round_pass<M, BF16, kRowsLoad>(Sb, sld, unused, unused, job, br, bc, valid, ls_steps, lds,
-                                       lds, none, unused, unused);
+                                       lds, none, unused);
         __syncthreads();
     }
 }
@@ -1876,7 +1978,6 @@ template <int M, bool BF16, bool POLISH>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(kSolveWaves<M>)))
 void batched_kernel(const MatJob* __restrict__ jobs, int count, int64_t total_groups, Params prm) {
     __shared__ __attribute__((aligned(16))) float lds[lds_floats<M>()];
-    float* slot = prm.scratch + (int64_t)blockIdx.x * kSlot<M>;
     for (int64_t g = blockIdx.x; g < total_groups; g += gridDim.x) {
         int lo = 0, hi = count - 1;
         while (lo < hi) {
@@ -1884,7 +1985,7 @@ void batched_kernel(const MatJob* __restrict__ jobs, int count, int64_t total_gr
             if (jobs[mid].group_begin <= g) lo = mid; else hi = mid - 1;
         }
         const MatJob job = jobs[lo];
-        process_group<M, BF16, POLISH>(job, prm, g - job.group_begin, slot, lds);
+        process_group<M, BF16, POLISH>(job, prm, g - job.group_begin, lds);
     }
 }
 
@@ -1929,16 +2030,6 @@ __global__ __launch_bounds__(256) void nonfinite_kernel(const void* __restrict__
             default: return (int)hipErrorInvalidValue;                  \
         }                                                               \
     } while (0)
-
-int64_t slot_floats(int M) {
-    switch (M) {
-        case 4: return kSlot<4>;
-        case 8: return kSlot<8>;
-        case 16: return kSlot<16>;
-        case 32: return kSlot<32>;
-        default: return 0;
-    }
-}
 
 int blocks_per_group(int M) {
     switch (M) {

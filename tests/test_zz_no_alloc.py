@@ -4,9 +4,8 @@ tsenor_mask, called through the C ABI on the same seeded inputs.
 Both entry points run the same kernels, so the masks must be bit-identical and
 S identical (the fractional-S bar is 1e-4; equality is asserted).  The calls
 run back to back on one stream: a large 16:32 call, a smaller 16:32 call and a
-smaller 4:8 fp32 call, so that each call finds the fixed workspace holding the
-previous call's data.  Every result is also checked for feasibility and
-against the oracle's rounding of its own S.
+smaller 4:8 fp32 call, each right after a larger one.  Every result is also
+checked for feasibility and against the oracle's rounding of its own S.
 """
 import ctypes
 
