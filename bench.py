@@ -149,10 +149,18 @@ def cpu_baseline(w, W_np, seconds):
     oracle.build(force=False)
     cores = oracle.max_threads()
     nbr = w.rows // w.M
-    t1, n1 = run(1, cores)
-    full = t1 * nbr <= 1.5 * seconds
-    k = nbr if full else int(max(1, min(nbr, round(seconds / max(t1, 1e-3)))))
-    t, n, reps = repeated(k, cores, min(10.0, seconds), first=(t1, n1) if k == 1 else None)
+    # Rate probe: the first block-row, then 4x as many until the probe runs at
+    # least 0.25 s (a single short block-row is mostly per-call overhead, which
+    # would make the whole matrix look dearer than it is).
+    kp = 1
+    tp, np_ = run(kp, cores)
+    while tp < 0.25 and kp < nbr:
+        kp = min(nbr, 4 * kp)
+        tp, np_ = run(kp, cores)
+    per_row = tp / kp
+    full = per_row * nbr <= 1.5 * seconds
+    k = nbr if full else int(max(1, min(nbr, round(seconds / max(per_row, 1e-3)))))
+    t, n, reps = repeated(k, cores, min(10.0, seconds), first=(tp, np_) if k == kp else None)
     ts, ns, reps1 = repeated(1, 1, 1.0)
     oracle.dykstra(np.zeros((w.M, w.M), np.float32), 1, w.M, 0.0, 1, nthreads=cores)  # restore
     what = (f"the whole matrix: {w.rows} x {w.cols} = {n // reps} weights, {w.blocks} blocks"

@@ -306,6 +306,23 @@ __device__ __forceinline__ float swz(float x) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), PAT));
 }
 
+// Register-level grouping point for the first K values of x: every write of
+// them precedes it and every later read follows it.  Emits no instruction.
+// The M = 16 column chain uses it to issue its adds, DPP adds and reciprocals
+// as three back-to-back runs: each switch between plain VALU instructions and
+// DPP or transcendental ones costs the wave issue time, and left alone the
+// scheduler interleaves the three kinds (8:16 -0.7%; at M = 32 it measured
+// the same or slower and is not used there).
+template <int K>
+__device__ __forceinline__ void group_fence(float (&x)[16]) {
+    static_assert(K == 4 || K == 8, "group size");
+    if constexpr (K == 8)
+        asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]),
+                          "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
+    else
+        asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+}
+
 // Butterfly (M = 16 and 32): on return x[0..3] of every lane hold the column
 // totals (max or sum over the 4 row groups) of those register columns; each
 // column is owned by exactly one lane of the block per row half.  The eight
@@ -321,11 +338,13 @@ __device__ __forceinline__ void col_reduce_scatter(float (&x)[16]) {
     for (int c = 0; c < 8; ++c) y[c] = swz<kSwzG1<M>>(x[c + 8]);
 #pragma unroll
     for (int c = 0; c < 8; ++c) x[c] = MAXOP ? fmaxf(x[c], y[c]) : x[c] + y[c];
+    if constexpr (M == 16) group_fence<8>(x);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         const float z = dpp_mov<kCtlG0<M>>(x[c + 4]);
         x[c] = MAXOP ? fmaxf(x[c], z) : x[c] + z;
     }
+    if constexpr (M == 16) group_fence<4>(x);
 }
 template <int G, bool MAXOP>
 __device__ __forceinline__ void col_pair_allreduce(float (&x)[4]) {
@@ -616,8 +635,12 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                 set_prio<kPrioChain>();
                 const float rs = ((acc0[0] + acc0[1]) + (acc0[2] + acc0[3])) +
                                  dpp_mov<Lanes32::kRow>((acc1[0] + acc1[1]) + (acc1[2] + acc1[3]));
-                const float a0 = fN * rcpf(rs);
-                const float a1 = dpp_mov<Lanes32::kRow>(a0);
+                // The partner's factor is formed from its reciprocal moved here:
+                // N * dpp(r) is one DPP multiply, where dpp(N * r) was a multiply,
+                // a DPP move and a wait state (same value; 16:32 -0.5%, tau 200
+                // -1.3%).
+                const float r0 = rcpf(rs);
+                const float a0 = fN * r0, a1 = fN * dpp_mov<Lanes32::kRow>(r0);
                 set_prio<0>();
                 U[r] *= a0;
                 U[r + 1] *= a1;
@@ -662,10 +685,14 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             // (a serial chain to the end of the cycle: raised priority)
             set_prio<kPrioChain>();
             col_reduce_scatter<M, false>(cacc);
+            float rc[16];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) rc[c] = rcpf(cacc[c]);
+            if constexpr (M == 16) group_fence<4>(rc);  // the 4 reciprocals back to back
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                if constexpr (H == 1) V[c] = V[c] * rcpf(cacc[c]);
-                else V[c] = V[c] * (fN * rcpf(cacc[c]));
+                if constexpr (H == 1) V[c] = V[c] * rc[c];
+                else V[c] = V[c] * (fN * rc[c]);
             }
             if ((it & 3) == 0) {
 #pragma unroll
