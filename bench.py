@@ -40,14 +40,14 @@ KERNEL_SOURCE = os.path.join(ROOT, "sparse_mask_search_amd", "csrc", "tsenor_ker
 # dispatch scaled by what the same counters read for a 1 GiB device copy (x 2.0
 # read, x 1.0 written), valid only for the kernel source they were taken on.  The
 # 7B-shaped model's entry sums its two launches.
-TRAFFIC_SHA = "7e5a34058378bf0679dcdbf3f2ec78a0f56158160fb9693b6267596d3989b27e"
+TRAFFIC_SHA = "e6ca3d106e0b76b7ce0d5ed396bd002b4a019a5990faece9adfcc7a3c3560eb9"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) in KiB per launch
-    "16:32-8192x28672-bf16": (470809.21875, 38838.625),
-    "16:32-8192x28672-bf16-tau200": (1995094.25, 48058.828125),
-    "8:16-4096x11008-bf16": (74973.28125, 5504.046875),
-    "4:8-4096x4096-f32": (52681.8125, 3072.0),
-    "2:4-1024x1024-f32": (2140.15625, 256.0),
-    "7b-model-batched": (8689485.1875 + 4177922.78125, 582410.65625 + 262144.0),
+    "16:32-8192x28672-bf16": (472015.25, 63943.71875),
+    "16:32-8192x28672-bf16-tau200": (556607.78125, 66661.3125),
+    "8:16-4096x11008-bf16": (68184.0625, 5834.9375),
+    "4:8-4096x4096-f32": (61739.46875, 3074.71875),
+    "2:4-1024x1024-f32": (2138.125, 256.0),
+    "7b-model-batched": (8645187.03125 + 3708148.84375, 954010.34375 + 262841.484375),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
