@@ -696,8 +696,18 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
                 else V[c] = V[c] * (fN * rc[c]);
             }
             if ((it & 3) == 0) {
+                if constexpr (M == 32) {
+                    // one range test of the extremes instead of one per scale
+                    // (-1% at 16:32; at M = 16 the per-scale tests measured
+                    // 2.7% faster and stay)
+                    float vlo = V[0], vhi = V[0];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) bad |= !(V[c] >= 0x1p-40f && V[c] <= 0x1p40f);
+                    for (int c = 1; c < 4; ++c) { vlo = fminf(vlo, V[c]); vhi = fmaxf(vhi, V[c]); }
+                    bad = !(vlo >= 0x1p-40f && vhi <= 0x1p40f);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) bad |= !(V[c] >= 0x1p-40f && V[c] <= 0x1p40f);
+                }
             }
             {
                 // The new scales reach the other lanes through LDS (one 16-byte
@@ -716,8 +726,15 @@ __device__ __forceinline__ void dykstra_group(const MatJob& job, const Params& p
             }
         }
         if ((it & 3) != 0) continue;
+        if constexpr (M == 32) {
+            float ulo = U[0], uhi = U[0];
 #pragma unroll
-        for (int r = 0; r < R; ++r) bad |= !(U[r] >= 0x1p-40f && U[r] <= 0x1p40f);
+            for (int r = 1; r < R; ++r) { ulo = fminf(ulo, U[r]); uhi = fmaxf(uhi, U[r]); }
+            bad |= !(ulo >= 0x1p-40f && uhi <= 0x1p40f);
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) bad |= !(U[r] >= 0x1p-40f && U[r] <= 0x1p40f);
+        }
         bad = bad && valid;
         if (__builtin_expect(__ballot(bad) != 0ull, 0)) {
             // Rare: fold the scales into the kernel (scales <- 1), so that
