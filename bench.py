@@ -40,14 +40,14 @@ KERNEL_SOURCE = os.path.join(ROOT, "sparse_mask_search_amd", "csrc", "tsenor_ker
 # dispatch scaled by what the same counters read for a 1 GiB device copy (x 2.0
 # read, x 1.0 written), valid only for the kernel source they were taken on.  The
 # 7B-shaped model's entry sums its two launches.
-TRAFFIC_SHA = "e6ca3d106e0b76b7ce0d5ed396bd002b4a019a5990faece9adfcc7a3c3560eb9"
+TRAFFIC_SHA = "5e338c8f5713e84d4c80eaf86abdffed6abf0bf845c05765d9677c189c56de52"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) in KiB per launch
-    "16:32-8192x28672-bf16": (472015.25, 63943.71875),
-    "16:32-8192x28672-bf16-tau200": (556607.78125, 66661.3125),
-    "8:16-4096x11008-bf16": (68184.0625, 5834.9375),
-    "4:8-4096x4096-f32": (61739.46875, 3074.71875),
-    "2:4-1024x1024-f32": (2138.125, 256.0),
-    "7b-model-batched": (8645187.03125 + 3708148.84375, 954010.34375 + 262841.484375),
+    "16:32-8192x28672-bf16": (471743.25, 63627.75),
+    "16:32-8192x28672-bf16-tau200": (548924.90625, 66729.796875),
+    "8:16-4096x11008-bf16": (68355.4375, 5834.125),
+    "4:8-4096x4096-f32": (61779.0, 3074.484375),
+    "2:4-1024x1024-f32": (2140.4375, 256.0),
+    "7b-model-batched": (8639829.65625 + 3712118.34375, 955526.390625 + 262825.0625),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
