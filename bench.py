@@ -40,14 +40,14 @@ KERNEL_SOURCE = os.path.join(ROOT, "sparse_mask_search_amd", "csrc", "tsenor_ker
 # dispatch scaled by what the same counters read for a 1 GiB device copy (x 2.0
 # read, x 1.0 written), valid only for the kernel source they were taken on.  The
 # 7B-shaped model's entry sums its two launches.
-TRAFFIC_SHA = "5e338c8f5713e84d4c80eaf86abdffed6abf0bf845c05765d9677c189c56de52"
+TRAFFIC_SHA = "17b7ab9157e5540d8343a4176867ce8f047cace810c0c9498b49fcf3ca872448"
 TRAFFIC_KIB = {  # workload: (FETCH_SIZE, WRITE_SIZE) in KiB per launch
-    "16:32-8192x28672-bf16": (471743.25, 63627.75),
-    "16:32-8192x28672-bf16-tau200": (548924.90625, 66729.796875),
-    "8:16-4096x11008-bf16": (68355.4375, 5834.125),
-    "4:8-4096x4096-f32": (61779.0, 3074.484375),
-    "2:4-1024x1024-f32": (2140.4375, 256.0),
-    "7b-model-batched": (8639829.65625 + 3712118.34375, 955526.390625 + 262825.0625),
+    "16:32-8192x28672-bf16": (471926.84375, 63500.328125),
+    "16:32-8192x28672-bf16-tau200": (550135.21875, 66092.765625),
+    "8:16-4096x11008-bf16": (68201.9375, 5832.796875),
+    "4:8-4096x4096-f32": (61764.21875, 3074.8125),
+    "2:4-1024x1024-f32": (2137.9375, 256.0),
+    "7b-model-batched": (8640354.3125 + 3712244.875, 953938.015625 + 262822.265625),
 }
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
