@@ -54,10 +54,15 @@
  *     lives in registers and LDS.  The library keeps a few cached buffers per
  *     device (the batched descriptor table, a copy of a previous mask that
  *     overlaps an output; allocated on first use, grown on demand, never
- *     freed before process exit).  Calls on one device other than
- *     tsenor_mask_noalloc are ordered: each launch follows the previous one
- *     on the device (stream event), so concurrent calls from any thread or
- *     stream are safe but do not overlap.  The host side is thread-safe.
+ *     freed before process exit).  Calls that can use one of these buffers
+ *     -- tsenor_mask_batched(_ex), tsenor_mask_ex with a previous mask that
+ *     overlaps its output -- and tsenor_round and tsenor_exact are ordered:
+ *     each launch follows the previous ordered one on the device (stream
+ *     event), so concurrent such calls from any thread or stream are safe but
+ *     do not overlap.  tsenor_mask, tsenor_mask_ex without such a previous
+ *     mask, and tsenor_mask_noalloc use no shared buffer and are not ordered:
+ *     calls on different streams may overlap in time (their outputs must not
+ *     overlap).  The host side is thread-safe.
  */
 #ifndef TSENOR_H
 #define TSENOR_H
